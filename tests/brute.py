@@ -1,0 +1,88 @@
+"""Brute-force attention with scalar Python loops, for pinning the oracle on tiny inputs.
+
+Written independently of ``oracle``: visible keys come from closed-form index
+ranges (not from boolean predicates over an index grid), every sum is
+``math.fsum`` and every exponential is ``math.exp``.  Only for inputs of a few
+dozen elements.
+
+A mask spec is a dict with any of:
+    causal: True               keys 0 .. p
+    window: (left, right)      keys p-left .. p+right (negative = unbounded)
+    docs: [len, ...]           keys of the document holding p
+    block: bs                  keys 0 .. (p // bs + 1) * bs - 1
+    tiles: (tile_map, T, inner_spec)   BlockMask over raw query index q
+    key_range: (lo, hi)        keys lo .. hi - 1
+with p = q + (Nk - Nq).
+"""
+import math
+
+
+def _range_keys(spec, q, Nq, Nk):
+    p = q + (Nk - Nq)
+    keys = set(range(Nk))
+    if spec.get("causal"):
+        keys &= set(range(0, min(Nk, p + 1)))
+    if "window" in spec:
+        left, right = spec["window"]
+        lo = 0 if left < 0 else max(0, p - left)
+        hi = Nk - 1 if right < 0 else min(Nk - 1, p + right)
+        keys &= set(range(lo, hi + 1))
+    if "docs" in spec:
+        start = 0
+        doc = set()
+        for ln in spec["docs"]:
+            if start <= p < start + ln:
+                doc = set(range(start, start + ln))
+            start += ln
+        keys &= doc
+    if "block" in spec:
+        bs = spec["block"]
+        keys &= set(range(0, min(Nk, (p // bs + 1) * bs)))
+    if "key_range" in spec:
+        lo, hi = spec["key_range"]
+        keys &= set(range(lo, hi))
+    if "tiles" in spec:
+        tmap, T, inner = spec["tiles"]
+        inner_keys = set(_range_keys(inner, q, Nq, Nk))
+        allowed = set()
+        for kt in range(len(tmap[0])):
+            state = int(tmap[q // T][kt])
+            tile_keys = set(range(kt * T, min(Nk, (kt + 1) * T)))
+            if state == 2:
+                allowed |= tile_keys
+            elif state == 1:
+                allowed |= tile_keys & inner_keys
+        keys &= allowed
+    return sorted(keys)
+
+
+def attention(q, k, v, scale, spec):
+    """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) nested lists."""
+    B, Hq = len(q), len(q[0])
+    Hkv = len(k[0])
+    Nq, Nk = len(q[0][0]), len(k[0][0])
+    G = Hq // Hkv
+    O, L = [], []
+    for b in range(B):
+        Ob, Lb = [], []
+        for h in range(Hq):
+            kv = h // G
+            Oh, Lh = [], []
+            for i in range(Nq):
+                keys = _range_keys(spec, i, Nq, Nk)
+                dv = len(v[b][kv][0]) if Nk else len(q[b][h][i])
+                if not keys:
+                    Oh.append([0.0] * dv)
+                    Lh.append(-math.inf)
+                    continue
+                s = {j: scale * math.fsum(a * c for a, c in zip(q[b][h][i], k[b][kv][j])) for j in keys}
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                tot = math.fsum(e.values())
+                Oh.append([math.fsum(e[j] * v[b][kv][j][d] for j in keys) / tot for d in range(dv)])
+                Lh.append(m + math.log(tot))
+            Ob.append(Oh)
+            Lb.append(Lh)
+        O.append(Ob)
+        L.append(Lb)
+    return O, L

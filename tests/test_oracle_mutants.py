@@ -1,0 +1,143 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each.
+
+Every mutant replaces one oracle function for the duration of a test; the pin
+suite of test_oracle_pins.py must then fail somewhere.  This shows the pins are
+strong enough that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle cannot go unnoticed.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import core as OA, masks as M, paged as OP, blockmask as OB
+import test_oracle_pins as P
+
+PINS = [
+    lambda: [P.pin_brute(c) for c in P.BRUTE_CASES],
+    P.pin_sdpa_causal, P.pin_sdpa_window_docs, P.pin_sdpa_block, P.pin_sdpa_tiles_gqa,
+    P.pin_sdpa_decode_paged, P.pin_probs_sum_to_one, P.pin_constant_v, P.pin_one_visible_key,
+    P.pin_q0_counts, P.pin_identities, P.pin_split_combine, P.pin_paged_equals_contiguous,
+    P.pin_blockmask_classes, P.test_hand_worked_golden, P.test_brute_force_paged_two_splits,
+]
+
+
+def _caught():
+    for pin in PINS:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+def _scores_no_scale(q_rows, k, scale):
+    return np.asarray(q_rows, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T
+
+
+def _softmax_lse_no_max(s, visible):
+    p, lse = _orig_softmax(s, visible)
+    s2 = np.where(visible, s, -np.inf)
+    m = np.max(s2, axis=-1)
+    return p, np.where(np.isfinite(m), lse - m, lse)
+
+
+def _softmax_sign(s, visible):
+    return _orig_softmax(-s, visible)
+
+
+def _causal_off_by_one(Nq, Nk):
+    def mod(b, h, q_idx, kv_idx):
+        return np.asarray(kv_idx) < np.asarray(q_idx) + (Nk - Nq)
+    return mod
+
+
+def _causal_top_left(Nq, Nk):
+    def mod(b, h, q_idx, kv_idx):
+        return np.asarray(kv_idx) <= np.asarray(q_idx)
+    return mod
+
+
+def _window_exclusive(left, right, Nq, Nk):
+    def mod(b, h, q_idx, kv_idx):
+        p = np.asarray(q_idx) + (Nk - Nq)
+        k = np.asarray(kv_idx)
+        return (k > p - left) & (k <= p + right)
+    return mod
+
+
+def _block_causal_strict(bs, Nq, Nk):
+    def mod(b, h, q_idx, kv_idx):
+        p = np.asarray(q_idx) + (Nk - Nq)
+        return (np.asarray(kv_idx) // bs) < (p // bs) + (np.asarray(kv_idx) % bs == 0)
+    return mod
+
+
+def _combine_unweighted(o_parts, lse_parts, axis=0):
+    o, lse = _orig_combine(o_parts, lse_parts, axis)
+    return np.mean(np.asarray(o_parts), axis=axis), lse
+
+
+def _gather_swapped(pool, block_table, b, seq_len):
+    pool = np.asarray(pool)
+    bt = np.asarray(block_table)
+    P = pool.shape[1]
+    j = np.arange(seq_len)
+    rows = pool[bt[b, j % bt.shape[1]], (j // P) % P]
+    return np.transpose(rows, (1, 0, 2))
+
+
+def _blockmask_full_masked(tile_map, tile, partial_mod):
+    def mod(b, h, q_idx, kv_idx):
+        tm = np.asarray(tile_map)
+        tm = tm if tm.ndim == 2 else tm[0, 0]
+        st = tm[np.asarray(q_idx) // tile, np.asarray(kv_idx) // tile]
+        return (st >= 1) & partial_mod(b, h, q_idx, kv_idx)
+    return mod
+
+
+_orig_softmax = OA.masked_softmax
+_orig_combine = OA.combine
+
+
+def _attention_rows_gqa_modulo(q, k, v, scale, mask_mod, b, hq, rows):
+    Hkv = k.shape[1]
+    kk = np.asarray(k)[:, [hq % Hkv] * k.shape[1]]
+    vv = np.asarray(v)[:, [hq % Hkv] * k.shape[1]]
+    G = q.shape[1] // Hkv
+    return _orig_rows(q, kk, vv, scale, mask_mod, b, (hq % Hkv) * G, rows)
+
+
+def _attention_rows_kv_swapped(q, k, v, scale, mask_mod, b, hq, rows):
+    return _orig_rows(q, v, k, scale, mask_mod, b, hq, rows)
+
+
+_orig_rows = OA.attention_rows
+
+MUTANTS = {
+    "scale_dropped": (OA, "scores", _scores_no_scale),
+    "lse_without_max": (OA, "masked_softmax", _softmax_lse_no_max),
+    "score_sign": (OA, "masked_softmax", _softmax_sign),
+    "causal_off_by_one": (M, "causal", _causal_off_by_one),
+    "causal_top_left": (M, "causal", _causal_top_left),
+    "window_exclusive": (M, "window", _window_exclusive),
+    "block_causal_wrong": (M, "block_causal", _block_causal_strict),
+    "combine_unweighted": (OA, "combine", _combine_unweighted),
+    "paged_index_swapped": (OP, "gather", _gather_swapped),
+    "blockmask_full_tiles_masked": (M, "blockmask", _blockmask_full_masked),
+    "gqa_modulo_mapping": (OA, "attention_rows", _attention_rows_gqa_modulo),
+    "k_v_transposed": (OA, "attention_rows", _attention_rows_kv_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    mod, attr, repl = MUTANTS[name]
+    monkeypatch.setattr(mod, attr, repl)
+    # functions re-exported at package level are patched too
+    if hasattr(oracle, attr) and mod is OA:
+        monkeypatch.setattr(oracle, attr, repl)
+    assert _caught(), f"no pin caught mutant {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    assert not _caught()
