@@ -1,0 +1,234 @@
+/*
+ * tiled_attn.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * What the library computes, for every batch row b and query head hq:
+ *
+ *     s[q, k] = scale * <Q[b, hq, q, :], K[b, kvh, k, :]>,   kvh = hq / (Hq / Hkv)
+ *     O[b, hq, q, :] = sum over visible k of softmax_k(s[q, k]) * V[b, kvh, k, :]
+ *     LSE[b, hq, q]  = log sum over visible k of exp(s[q, k])       (natural log)
+ *
+ * the plain attention softmax(QK^T / sqrt(d)) V of "FlashAttention 2 principles
+ * and PyTorch practice" (section 1), computed the way its sections 1 and 3
+ * describe: Q in blocks, K/V streamed block by block through on-chip memory,
+ * an online softmax (running max and exp-sum, accumulator rescaled), so the
+ * N x N score matrix never reaches HBM.  Which keys a query sees comes from
+ * the mask menu of the FlexAttention / DFlash article (section 1: mask_mod,
+ * BlockMask, GQA, split-KV decoding over a paged cache; section 3: the
+ * symmetric sliding window).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Q, K, V, O are bfloat16 (the kernel dtype the FlashAttention 2 article,
+ *   section 7, asks for; fp32 callers convert first).  Accumulation is fp32.
+ * - Tensors are logical [B, H, N, D] with D contiguous (stride 1).  Each
+ *   tensor comes with three element strides for (b, h, n); any order of the
+ *   B/H/N dimensions in memory is accepted, so both [B, H, N, D] and
+ *   [B, N, H, D] layouts pass without a copy (FlashAttention 2 article,
+ *   section 2).  Strides must be multiples of 8 elements and base pointers
+ *   16-byte aligned.
+ * - LSE is fp32 [B, Hq, Nq], contiguous, natural log, scale included.  A row
+ *   that sees no key gets O = 0 and LSE = -inf.  LSE pointers may be NULL
+ *   where noted (then it is not written).
+ * - D is 64 or 128.  Hq must be a multiple of Hkv (GQA, consecutive
+ *   grouping: query head hq reads KV head hq / (Hq / Hkv)).
+ * - scale must be finite and > 0 (callers wanting 1/sqrt(D) pass it).
+ * - Every pointer to tensor data is a DEVICE pointer owned by the caller.
+ *   The library allocates nothing, frees nothing, keeps no state between
+ *   calls and never synchronises: each call validates its arguments on the
+ *   host, then enqueues its kernels on `stream` and returns.
+ * - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code.  Arguments are
+ *   checked before any launch; on an error nothing is launched and no output
+ *   is touched.  ATTN_ERR_LAUNCH reports hipGetLastError() after a launch.
+ * - Results are deterministic: no atomics in any reduction; the reduction
+ *   order depends only on logical positions, never on memory placement.
+ */
+#ifndef TILED_ATTN_H
+#define TILED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define ATTN_OK 0
+#define ATTN_ERR_NULL (-1)      /* a required pointer is NULL                  */
+#define ATTN_ERR_SHAPE (-2)     /* negative size, or a size over a limit       */
+#define ATTN_ERR_HEAD_DIM (-3)  /* D is not 64 or 128                          */
+#define ATTN_ERR_GQA (-4)       /* Hq not a positive multiple of Hkv           */
+#define ATTN_ERR_STRIDE (-5)    /* stride not a multiple of 8 elements         */
+#define ATTN_ERR_ALIGN (-6)     /* tensor base not 16-byte aligned             */
+#define ATTN_ERR_MASK (-7)      /* unknown mask flag or bad mask parameter     */
+#define ATTN_ERR_WORKSPACE (-8) /* workspace / split arguments inconsistent    */
+#define ATTN_ERR_LAUNCH (-9)    /* the HIP runtime reported a launch error     */
+#define ATTN_ERR_BLOCKMASK (-10)/* BlockMask descriptor inconsistent           */
+#define ATTN_ERR_SCALE (-11)    /* scale not finite and > 0                    */
+
+/* ---- masks --------------------------------------------------------------
+ * A query row q is placed at the absolute position p = q + (Nk - Nq)
+ * (bottom-right alignment; the FlashAttention 2 article, section 7, warns
+ * that a misaligned causal mask shifts the output).  The flags are
+ * AND-composed; flags == 0 means every key is visible (non-causal /
+ * bidirectional).  Every flag keeps the visible keys of a row one contiguous
+ * interval [lo(p), hi(p)], and both ends never decrease as p grows.
+ */
+#define ATTN_MASK_CAUSAL 1u       /* k <= p                                       */
+#define ATTN_MASK_WINDOW 2u       /* p - window_left <= k <= p + window_right     */
+#define ATTN_MASK_DOCUMENT 4u     /* k in the same document as p                  */
+#define ATTN_MASK_BLOCK_CAUSAL 8u /* k < block_size * (p / block_size + 1)        */
+#define ATTN_MASK_ALL 15u
+
+typedef struct attn_mask_desc {
+  uint32_t flags;       /* ATTN_MASK_* bits                                        */
+  int32_t window_left;  /* WINDOW: inclusive widths; a negative width leaves that  */
+  int32_t window_right; /*   side unbounded.  Symmetric (w, w) is the pages' case. */
+  int32_t block_size;   /* BLOCK_CAUSAL: block length (> 0)                        */
+  /* DOCUMENT: device int32 [B][doc_stride] of cumulative document starts.
+   * Row b holds num_docs + 1 entries: doc d covers keys [off[d], off[d+1]).
+   * off[0] = 0, non-decreasing, off[num_docs] = Nk; rows with fewer documents
+   * repeat their final offset.  DOCUMENT requires Nq <= Nk (every query
+   * position then lies inside the key sequence).  Offsets that break these
+   * rules give unspecified values but never an out-of-range access
+   * (positions are clamped to [0, Nk)).                                         */
+  const int32_t* doc_offsets;
+  int32_t num_docs;     /* documents per row (>= 1)                                */
+  int32_t doc_stride;   /* elements between rows of doc_offsets (>= num_docs + 1)  */
+} attn_mask_desc;
+
+/* ---- dense-mask prefill ---------------------------------------------------
+ * attn_fwd: O = softmax(scale * Q K^T restricted by `mask`) V, plus LSE.
+ *   q  [B, Hq,  Nq, D], k/v [B, Hkv, Nk, D], o [B, Hq, Nq, D] (strides (b,h,n))
+ *   lse float [B, Hq, Nq] contiguous, or NULL.
+ *   mask may be NULL (no mask).  Nq or Nk may be 0 (Nk = 0: every row empty;
+ *   k and v may then be NULL).
+ * The key blocks of a query block are chosen analytically from the mask's
+ * per-row intervals: blocks outside every row's interval are skipped, blocks
+ * inside every row's interval run unmasked, the rest apply the interval
+ * per element in registers.
+ */
+int attn_fwd(const void* q, const int64_t q_stride[3],
+             const void* k, const int64_t k_stride[3],
+             const void* v, const int64_t v_stride[3],
+             void* o, const int64_t o_stride[3], float* lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             const attn_mask_desc* mask, hipStream_t stream);
+
+/* ---- BlockMask -----------------------------------------------------------
+ * Block-level sparsity over 128 x 128 tiles (FlexAttention article,
+ * section 1).  Per (batch row, head, query tile) the BlockMask lists the key
+ * tiles to visit: FULL tiles run with no predicate, PARTIAL tiles apply the
+ * `mask` intervals per element, tiles in neither list are skipped.
+ * Bm / Hm are 1 when one BlockMask is shared by every batch row / head.
+ */
+#define ATTN_BLOCKMASK_TILE 128
+#define ATTN_TILE_EMPTY 0
+#define ATTN_TILE_PARTIAL 1
+#define ATTN_TILE_FULL 2
+
+typedef struct attn_blockmask {
+  int32_t Bm, Hm;     /* 1 (shared) or B / Hq                                   */
+  int32_t nQt, nKt;   /* ceil(Nq / 128), ceil(Nk / 128)                          */
+  int32_t* part_num;  /* device [Bm][Hm][nQt]: number of PARTIAL tiles           */
+  int32_t* part_idx;  /* device [Bm][Hm][nQt][nKt]: their key-tile indices, ascending */
+  int32_t* full_num;  /* device [Bm][Hm][nQt]                                    */
+  int32_t* full_idx;  /* device [Bm][Hm][nQt][nKt]                               */
+} attn_blockmask;
+
+/* Bytes of device memory the four arrays of one attn_blockmask need in total
+ * (the caller allocates them; 0 on invalid sizes). */
+size_t attn_blockmask_bytes(int Bm, int Hm, int nQt, int nKt);
+
+/* attn_build_blockmask: fills `out` (whose pointers and Bm, Hm, nQt, nKt the
+ * caller has set) on `stream`.
+ *   tile_map: device uint8 [Bm][Hm][nQt][nKt] of ATTN_TILE_* codes, or NULL.
+ *     Given: each tile takes its class from the map (the `mask` predicate is
+ *     applied to PARTIAL tiles at attention time, FlexAttention semantics).
+ *     NULL: classes come from `mask` (required then): a tile is EMPTY when no
+ *     in-range (q, k) pair of it is visible, FULL when every in-range pair is,
+ *     PARTIAL otherwise.  With a DOCUMENT mask Bm must equal B.
+ *   B is the batch size the mask's doc_offsets describe (ignored otherwise).
+ * Lists are written in ascending key-tile order; entries past a row's count
+ * are set to 0, so the output is fully determined.
+ */
+int attn_build_blockmask(const attn_mask_desc* mask, const uint8_t* tile_map,
+                         int B, int Nq, int Nk, attn_blockmask* out,
+                         hipStream_t stream);
+
+/* attn_fwd_blockmask: attn_fwd restricted to the tiles `bm` lists.
+ * bm->nQt / nKt must equal ceil(Nq/128) / ceil(Nk/128); bm->Bm in {1, B},
+ * bm->Hm in {1, Hq}.  `mask` (may be NULL) is applied on PARTIAL tiles only.
+ */
+int attn_fwd_blockmask(const void* q, const int64_t q_stride[3],
+                       const void* k, const int64_t k_stride[3],
+                       const void* v, const int64_t v_stride[3],
+                       void* o, const int64_t o_stride[3], float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+                       const attn_mask_desc* mask, const attn_blockmask* bm,
+                       hipStream_t stream);
+
+/* ---- split-KV paged decode -------------------------------------------------
+ * "Short query, long KV" decoding split over the key sequence and merged by
+ * log-sum-exp (FlexAttention article, section 1: FlashDecoding-style split-KV
+ * with GQA and a paged cache addressed through a block table).
+ *
+ * attn_decode_splitkv: for each sequence b, KV head, split s and query row,
+ * the attention over split s's keys only, normalised, in fp32:
+ *   q           [B, Hq, Lq, D] bf16 (strides (b, h, n))
+ *   k_cache,    [num_pages, page_size, Hkv, D] bf16, contiguous pool
+ *   v_cache
+ *   block_table device int32 [B][bt_stride]; logical key j of sequence b
+ *               lives in page block_table[b][j / page_size], slot j % page_size
+ *   seq_lens    device int32 [B]: key count of each sequence, the Lq new
+ *               tokens included (0 <= seq_lens[b] <= max_pages * page_size)
+ *   max_pages   pages of the block table a sequence may use (<= bt_stride)
+ *   num_splits  S >= 1.  Split s covers keys [s*C, min((s+1)*C, seq_len))
+ *               with C = page_size * ceil(max_pages / S).
+ *   mask        NULL = causal; else CAUSAL / WINDOW / BLOCK_CAUSAL flags
+ *               (DOCUMENT is rejected).  Query t of sequence b sits at
+ *               position seq_lens[b] - Lq + t.
+ *   ws_o        float [B][Hq][Lq][S][D] (caller-allocated workspace)
+ *   ws_lse      float [B][Hq][Lq][S]
+ * A split with no visible key writes O_s = 0, LSE_s = -inf.  Pages past a
+ * sequence's length are never read.  Out-of-contract inputs give unspecified
+ * values but no out-of-range access: seq_lens are clamped to
+ * [0, max_pages * page_size] and page indices to [0, num_pages).
+ */
+int attn_decode_splitkv(const void* q, const int64_t q_stride[3],
+                        const void* k_cache, const void* v_cache, int64_t num_pages,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* seq_lens, int max_pages,
+                        int B, int Hq, int Hkv, int Lq, int D, int page_size,
+                        int num_splits, float scale, const attn_mask_desc* mask,
+                        float* ws_o, float* ws_lse, hipStream_t stream);
+
+/* attn_decode_combine: O = sum_s exp(LSE_s - LSE) O_s with
+ * LSE = log sum_s exp(LSE_s) (max-shifted); splits with LSE_s = -inf weigh 0.
+ *   o   [B, Hq, Lq, D] bf16 (strides (b, h, n)); lse float [B, Hq, Lq] or NULL.
+ */
+int attn_decode_combine(const float* ws_o, const float* ws_lse,
+                        int B, int Hq, int Lq, int S, int D,
+                        void* o, const int64_t o_stride[3], float* lse,
+                        hipStream_t stream);
+
+/* Workspace sizes of attn_decode_splitkv in bytes (0 on invalid sizes). */
+size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits);
+size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits);
+
+/* A split count that fills the GPU: enough (sequence, KV head, split) work
+ * groups for every compute unit, never more splits than pages. */
+int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
+
+/* Human-readable text of a status code (static storage). */
+const char* attn_status_str(int status);
+
+/* ABI version, bumped on any signature or semantic change. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_ATTN_H */

@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every symbol include/tiled_attn.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: no compute call
+is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tiled_attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def T():
+    import tiled_attention_attn_amd as T
+    return T
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_decode_splitkv",
+              "attn_decode_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(T):
+    lib = ctypes.CDLL(T.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(T.EXPORTS)
+
+
+def test_status_strings(T):
+    assert T.attn_status_str(0) == "ok"
+    for code in range(-11, 0):
+        assert T.attn_status_str(code) != "unknown status"
+    assert T.attn_abi_version() >= 1
+
+
+def _strides(*v):
+    return (ctypes.c_int64 * 3)(*v)
+
+
+def _fwd(T, **kw):
+    lib = T.lib_handle()
+    a = dict(q=16, k=32, v=48, o=64, qs=(64 * 256, 64 * 256, 64), ks=None, vs=None, os=None, lse=None,
+             B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, scale=0.125, mask=None)
+    a.update(kw)
+    s = lambda x: _strides(*(x or a["qs"]))
+    mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+    return lib.attn_fwd(a["q"], s(a["qs"]), a["k"], s(a["ks"]), a["v"], s(a["vs"]), a["o"], s(a["os"]),
+                        a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"], mk, None)
+
+
+def test_fwd_argument_errors(T):
+    # every case fails validation, so nothing is launched
+    assert _fwd(T, q=None) == -1
+    assert _fwd(T, k=None) == -1
+    assert _fwd(T, D=96) == -3
+    assert _fwd(T, Hq=3, Hkv=2) == -4
+    assert _fwd(T, Hkv=0) == -4
+    assert _fwd(T, qs=(64 * 256, 64 * 256, 60)) == -5
+    assert _fwd(T, q=18) == -6
+    assert _fwd(T, Nq=-1) == -2
+    assert _fwd(T, scale=0.0) == -11
+    assert _fwd(T, scale=float("nan")) == -11
+    m = T.attn_mask_desc(flags=64)
+    assert _fwd(T, mask=m) == -7
+    m = T.attn_mask_desc(flags=T.MASK_BLOCK_CAUSAL, block_size=0)
+    assert _fwd(T, mask=m) == -7
+    m = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=None, num_docs=1, doc_stride=2)
+    assert _fwd(T, mask=m) == -1
+    m = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=1024, num_docs=2, doc_stride=2)
+    assert _fwd(T, mask=m) == -7
+    m = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=1024, num_docs=1, doc_stride=2)
+    assert _fwd(T, mask=m, Nq=300, Nk=256) == -7
+
+
+def test_empty_problems_launch_nothing(T):
+    # B = 0 or Nq = 0: valid, nothing to do, returns OK without touching the GPU
+    assert _fwd(T, B=0) == 0
+    assert _fwd(T, Nq=0) == 0
+
+
+def test_blockmask_and_decode_argument_errors(T):
+    lib = T.lib_handle()
+    bm = T.attn_blockmask(Bm=1, Hm=1, nQt=2, nKt=2, part_num=16, part_idx=32, full_num=48, full_idx=64)
+    assert lib.attn_build_blockmask(None, None, 1, 256, 256, ctypes.byref(bm), None) == -1  # no map, no mask
+    bad = T.attn_blockmask(Bm=1, Hm=1, nQt=3, nKt=2, part_num=16, part_idx=32, full_num=48, full_idx=64)
+    m = T.attn_mask_desc(flags=T.MASK_CAUSAL)
+    assert lib.attn_build_blockmask(ctypes.byref(m), None, 1, 256, 256, ctypes.byref(bad), None) == -10
+    assert lib.attn_blockmask_bytes(1, 1, 2, 2) == 2 * 4 * 2 + 2 * 2 * 4 * 2
+    qs = _strides(32 * 16 * 128, 16 * 128, 128)
+    args = lambda **kw: dict(dict(q=16, qs=qs, kc=32, vc=48, pages=10, bt=64, bts=4, sl=80, maxp=4, B=1,
+                                  Hq=4, Hkv=2, Lq=2, D=128, ps=16, S=2, scale=0.1, mask=None, wo=96, wl=112), **kw)
+
+    def dec(**kw):
+        a = args(**kw)
+        mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+        return lib.attn_decode_splitkv(a["q"], a["qs"], a["kc"], a["vc"], a["pages"], a["bt"], a["bts"],
+                                       a["sl"], a["maxp"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"],
+                                       a["ps"], a["S"], a["scale"], mk, a["wo"], a["wl"], None)
+    assert dec(wo=None) == -1
+    assert dec(S=0) == -8
+    assert dec(bts=3) == -2
+    assert dec(D=80) == -3
+    assert dec(Hq=3) == -4
+    md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=1, doc_stride=2)
+    assert dec(mask=md) == -7
+    assert dec(B=0) == 0
+    assert lib.attn_decode_combine(None, 16, 1, 1, 1, 1, 64, 32, qs, None, None) == -1
+    assert lib.attn_decode_combine(16, 16, 1, 1, 1, 0, 64, 32, qs, None, None) == -8
+    assert lib.attn_decode_num_splits(16, 8, 2048, 256) == 4
+    assert lib.attn_decode_num_splits(1, 1, 3, 256) == 3
+    assert lib.attn_decode_ws_o_bytes(16, 32, 16, 128, 4) == 16 * 32 * 16 * 4 * 128 * 4
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package and its C sources never import or include the oracle or the workloads."""
+    pkg = os.path.join(ROOT, "tiled_attention_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.replace("Oracle", ""), f
+                assert "import workloads" not in src and "from workloads" not in src, f

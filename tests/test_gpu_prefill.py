@@ -1,0 +1,243 @@
+"""GPU parity: attn_fwd (dense-mask prefill) against the fp64 CPU oracle."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import masks as M
+import workloads as W
+from gpu_util import (O_TOL, LSE_TOL, COUNT_LSE_TOL, f64, LazyF64, assert_close, sample_rows,
+                      doc_offsets, announce)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():  # on a GPU machine the HIP library must load: no fallback
+    import tiled_attention_attn_amd as T
+DEV = "cuda"
+
+
+def _mask_pair(spec, B, Nq, Nk, device=DEV):
+    """(GPU Mask, oracle mask_mod) for a spec dict."""
+    gm = T.Mask(causal=spec.get("causal", False), window=spec.get("window"),
+                block_size=spec.get("block"))
+    mods = []
+    if spec.get("causal"):
+        mods.append(M.causal(Nq, Nk))
+    if spec.get("window") is not None:
+        mods.append(M.window(spec["window"][0], spec["window"][1], Nq, Nk))
+    if spec.get("block") is not None:
+        mods.append(M.block_causal(spec["block"], Nq, Nk))
+    if spec.get("docs") is not None:
+        gm.doc_offsets = doc_offsets(spec["docs"], device)
+        mods.append(M.document(spec["docs"], Nq, Nk))
+    return gm, (M.and_(*mods) if mods else None)
+
+
+def _run(q, k, v, scale, gm, layout="bhnd"):
+    """q/k/v CPU bf16 [B,H,N,D]; returns (O, LSE) on the CPU."""
+    B, Hq, Nq, D = q.shape
+    if layout == "bnhd":
+        qg = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        kg = k.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        vg = v.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        o = torch.empty(B, Nq, Hq, D, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    else:
+        qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+        o = torch.empty_like(qg)
+    o.fill_(float("nan"))
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device=DEV)
+    T.attn_fwd(qg, kg, vg, o, lse, scale, gm)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+SMALL = [
+    # (id, B, Hq, Hkv, Nq, Nk, D, spec)
+    ("none_d64", 2, 2, 2, 200, 200, 64, {}),
+    ("causal_d64_n1", 1, 2, 2, 1, 1, 64, {"causal": True}),
+    ("causal_d64_n127", 2, 3, 3, 127, 127, 64, {"causal": True}),
+    ("causal_d64_n129", 1, 2, 2, 129, 129, 64, {"causal": True}),
+    ("causal_d64_n1000", 1, 2, 2, 1000, 1000, 64, {"causal": True}),
+    ("causal_d128_n1000", 1, 2, 2, 1000, 1000, 128, {"causal": True}),
+    ("causal_bottom_right", 2, 2, 2, 100, 700, 64, {"causal": True}),
+    ("causal_gqa_4_1", 1, 4, 1, 520, 520, 128, {"causal": True}),
+    ("window_sym_d128", 1, 2, 2, 777, 777, 128, {"window": (100, 100)}),
+    ("window_asym_d64", 1, 2, 2, 500, 500, 64, {"window": (37, 5)}),
+    ("window_docs_d128", 2, 2, 2, 900, 900, 128,
+     {"window": (64, 64), "docs": [[130, 400, 370], [900]]}),
+    ("docs_only_d64", 1, 2, 1, 600, 600, 64, {"docs": [[1, 255, 100, 244]]}),
+    ("block_diffusion_d128", 1, 2, 2, 600, 600, 128, {"block": 16}),
+    ("block_diffusion_d64_bs5", 1, 1, 1, 333, 333, 64, {"block": 5}),
+    ("causal_window_d64", 1, 2, 2, 640, 640, 64, {"causal": True, "window": (200, 0)}),
+    ("nonsquare_window", 1, 2, 2, 64, 1000, 128, {"window": (300, 20)}),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_vs_oracle(case):
+    name, B, Hq, Hkv, Nq, Nk, D, spec = case
+    announce(name)
+    g = W.generator(zlib.crc32(name.encode()) % 9973)
+    q = W.randn_bf16(g, (B, Hq, Nq, D))
+    k = W.randn_bf16(g, (B, Hkv, Nk, D))
+    v = W.randn_bf16(g, (B, Hkv, Nk, D))
+    scale = 1.0 / math.sqrt(D)
+    gm, mod = _mask_pair(spec, B, Nq, Nk)
+    o, lse = _run(q, k, v, scale, gm)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
+    assert_close(f64(o), f64(lse), ro, rl, name)
+
+
+@pytest.mark.parametrize("layout", ["bnhd"])
+def test_strided_layout(layout):
+    announce("bnhd layout")
+    g = W.generator(4)
+    q = W.randn_bf16(g, (2, 4, 300, 128))
+    k = W.randn_bf16(g, (2, 2, 300, 128))
+    v = W.randn_bf16(g, (2, 2, 300, 128))
+    gm, mod = _mask_pair({"causal": True}, 2, 300, 300)
+    o, lse = _run(q, k, v, 0.1, gm, layout)
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), 0.1, mod)
+    assert_close(f64(o), f64(lse), ro, rl, "bnhd")
+
+
+def test_config1_causal_b1h1n256d64():
+    """Single-head causal B=1 H=1 N=256 D=64, fp32 inputs quantised to bf16 (seed 0)."""
+    announce("causal_b1h1n256d64")
+    wl = W.causal_b1h1n256d64()
+    q, k, v = (wl.tensors[x] for x in ("q", "k", "v"))
+    o, lse = _run(q, k, v, wl.scale, T.Mask(causal=True))
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), wl.scale, M.causal(256, 256))
+    assert_close(f64(o), f64(lse), ro, rl, "config1")
+
+
+def _q0_counts(Nq, Nk, spec):
+    """Closed-form number of visible keys per row (bottom-right aligned)."""
+    p = np.arange(Nq) + (Nk - Nq)
+    lo = np.zeros(Nq, dtype=np.int64)
+    hi = np.full(Nq, Nk - 1, dtype=np.int64)
+    if spec.get("causal"):
+        hi = np.minimum(hi, p)
+    if spec.get("window") is not None:
+        wl, wr = spec["window"]
+        lo = np.maximum(lo, p - wl)
+        hi = np.minimum(hi, p + wr)
+    if spec.get("block") is not None:
+        bs = spec["block"]
+        hi = np.minimum(hi, (p // bs + 1) * bs - 1)
+    if spec.get("docs") is not None:
+        starts = np.concatenate([[0], np.cumsum(spec["docs"][0])])
+        d = np.searchsorted(starts, p, side="right") - 1
+        lo = np.maximum(lo, starts[d])
+        hi = np.minimum(hi, starts[d + 1] - 1)
+    return np.maximum(hi - lo + 1, 0)
+
+
+@pytest.mark.parametrize("spec", [{"causal": True}, {"window": (512, 512), "docs": "cfg"},
+                                  {"block": 16}], ids=["causal", "window_docs", "block16"])
+def test_q0_lse_counts_exact(spec):
+    """Q = 0: every visible score is 0, so LSE = ln(#visible) exactly; this detects a single
+    missing or extra key, which the 1e-3 LSE bar cannot at long N."""
+    N, D = 8192, 128
+    announce(f"q0 counts {spec}")
+    g = W.generator(7)
+    spec = dict(spec)
+    if spec.get("docs") == "cfg":
+        spec["docs"] = [W.doc_lengths(g, N)]
+    k = W.randn_bf16(g, (1, 2, N, D))
+    v = W.randn_bf16(g, (1, 2, N, D))
+    q = torch.zeros(1, 2, N, D, dtype=torch.bfloat16)
+    gm, _ = _mask_pair(spec, 1, N, N)
+    o, lse = _run(q, k, v, 0.1, gm)
+    cnt = _q0_counts(N, N, spec)
+    err = np.max(np.abs(f64(lse)[0] - np.log(cnt)[None]))
+    assert err <= COUNT_LSE_TOL, err
+    if spec.get("causal"):
+        # O = mean of the visible V rows
+        vv = f64(v)[0]
+        for r in (0, 1, 511, 4097, N - 1):
+            assert np.max(np.abs(f64(o)[0, :, r] - vv[:, : r + 1].mean(1))) <= O_TOL
+
+
+def test_empty_key_sequence():
+    announce("Nk = 0")
+    q = torch.randn(1, 2, 70, 64).to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16)
+    o, lse = _run(q, k, k.clone(), 0.125, None)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_fully_masked_rows():
+    """Nq > Nk with causal bottom-right alignment: the first Nq-Nk rows see nothing."""
+    announce("fully masked rows")
+    g = W.generator(8)
+    q = W.randn_bf16(g, (1, 1, 200, 64))
+    k = W.randn_bf16(g, (1, 1, 150, 64))
+    v = W.randn_bf16(g, (1, 1, 150, 64))
+    o, lse = _run(q, k, v, 0.125, T.Mask(causal=True))
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), 0.125, M.causal(200, 150))
+    assert_close(f64(o), f64(lse), ro, rl, "masked rows")
+    assert torch.all(o[0, 0, :50] == 0) and torch.all(torch.isneginf(lse[0, 0, :50]))
+
+
+def test_config2_causal_b2h16n4096d64_sampled_and_deterministic():
+    """Causal prefill B=2 H=16 N=4096 D=64 at full size: sampled rows vs the oracle, and
+    two runs bitwise equal."""
+    announce("causal_b2h16n4096d64")
+    wl = W.causal_b2h16n4096d64()
+    q, k, v = (wl.tensors[x].to(DEV) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 16, 4096, dtype=torch.float32, device=DEV)
+    T.attn_fwd(q, k, v, o, lse, wl.scale, T.Mask(causal=True))
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty_like(lse)
+    T.attn_fwd(q, k, v, o2, lse2, wl.scale, T.Mask(causal=True))
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+    mod = M.causal(4096, 4096)
+    qa, ka, va = LazyF64(q), LazyF64(k), LazyF64(v)
+    for (b, h) in ((0, 0), (0, 7), (1, 15), (1, 3)):
+        rows = sample_rows(4096, 48, b * 16 + h)
+        ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, b, h, rows)
+        assert_close(f64(o[b, h, rows]), f64(lse[b, h, rows]), ro, rl, f"cfg2 b{b} h{h}")
+
+
+@pytest.mark.parametrize("variant", ["window_doc", "blockdiff"])
+def test_config3_b1h32n8192d128_sampled(variant):
+    name = "window_doc_b1h32n8192d128" if variant == "window_doc" else "blockdiff_b1h32n8192d128"
+    announce(name)
+    wl = W.FULL_SIZE[name]()
+    q, k, v = (wl.tensors[x].to(DEV) for x in ("q", "k", "v"))
+    m = wl.mask
+    spec = {"window": (m["window"], m["window"]), "docs": m["doc_lengths"]} if variant == "window_doc" \
+        else {"block": m["block_size"]}
+    gm, mod = _mask_pair(spec, 1, 8192, 8192)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 32, 8192, dtype=torch.float32, device=DEV)
+    T.attn_fwd(q, k, v, o, lse, wl.scale, gm)
+    torch.cuda.synchronize()
+    qa, ka, va = LazyF64(q), LazyF64(k), LazyF64(v)
+    for h in (0, 13, 31):
+        rows = sample_rows(8192, 64, h)
+        ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, 0, h, rows)
+        assert_close(f64(o[0, h, rows]), f64(lse[0, h, rows]), ro, rl, f"{name} h{h}")
+
+
+def test_golden_long_single_head_32768():
+    """Edge case L = 32768, single head causal (sampled rows)."""
+    announce("L=32768")
+    g = W.generator(11)
+    N, D = 32768, 64
+    q = W.randn_bf16(g, (1, 1, N, D)).to(DEV)
+    k = W.randn_bf16(g, (1, 1, N, D)).to(DEV)
+    v = W.randn_bf16(g, (1, 1, N, D)).to(DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 1, N, dtype=torch.float32, device=DEV)
+    T.attn_fwd(q, k, v, o, lse, 0.125, T.Mask(causal=True))
+    torch.cuda.synchronize()
+    rows = sample_rows(N, 32, 1)
+    ro, rl = oracle.attention_rows(LazyF64(q), LazyF64(k), LazyF64(v), 0.125, M.causal(N, N), 0, 0, rows)
+    assert_close(f64(o[0, 0, rows]), f64(lse[0, 0, rows]), ro, rl, "L=32768")

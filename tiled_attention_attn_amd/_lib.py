@@ -1,0 +1,308 @@
+"""ctypes binding of libtiled_attn.so (include/tiled_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI.  Functions keep the C names; torch tensors (on the
+GPU) supply the device pointers, shapes and element strides, and the current
+torch stream is used unless one is passed.  A non-zero status raises
+``AttnError`` with the library's own message.  If the library is missing the
+import fails: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtiled_attn.so")
+
+MASK_CAUSAL = 1
+MASK_WINDOW = 2
+MASK_DOCUMENT = 4
+MASK_BLOCK_CAUSAL = 8
+BLOCKMASK_TILE = 128
+TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
+
+
+class AttnError(RuntimeError):
+    def __init__(self, func: str, status: int, msg: str):
+        super().__init__(f"{func}: status {status}: {msg}")
+        self.status = status
+
+
+class attn_mask_desc(ctypes.Structure):
+    _fields_ = [
+        ("flags", ctypes.c_uint32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("doc_offsets", ctypes.c_void_p),
+        ("num_docs", ctypes.c_int32),
+        ("doc_stride", ctypes.c_int32),
+    ]
+
+
+class attn_blockmask(ctypes.Structure):
+    _fields_ = [
+        ("Bm", ctypes.c_int32), ("Hm", ctypes.c_int32),
+        ("nQt", ctypes.c_int32), ("nKt", ctypes.c_int32),
+        ("part_num", ctypes.c_void_p), ("part_idx", ctypes.c_void_p),
+        ("full_num", ctypes.c_void_p), ("full_idx", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    I64 = ctypes.c_int64
+    STR = ctypes.POINTER(ctypes.c_int64)
+    MP = ctypes.POINTER(attn_mask_desc)
+    BP = ctypes.POINTER(attn_blockmask)
+    sig = {
+        "attn_fwd": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, F, MP, P]),
+        "attn_fwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, F, MP, BP, P]),
+        "attn_build_blockmask": (I, [MP, P, I, I, I, BP, P]),
+        "attn_blockmask_bytes": (S, [I, I, I, I]),
+        "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, F, MP, P, P, P]),
+        "attn_decode_combine": (I, [P, P, I, I, I, I, I, P, STR, P, P]),
+        "attn_decode_ws_o_bytes": (S, [I, I, I, I, I]),
+        "attn_decode_ws_lse_bytes": (S, [I, I, I, I]),
+        "attn_decode_num_splits": (I, [I, I, I, I]),
+        "attn_status_str": (ctypes.c_char_p, [I]),
+        "attn_abi_version": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_blockmask_bytes",
+           "attn_decode_splitkv", "attn_decode_combine", "attn_decode_ws_o_bytes",
+           "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_status_str",
+           "attn_abi_version")
+
+
+def _check(func: str, status: int):
+    if status != 0:
+        raise AttnError(func, status, _lib.attn_status_str(status).decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _strides(t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-d [B, H, N, D] tensor")
+    arr = (ctypes.c_int64 * 3)(*t.stride()[:3])
+    return arr
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("Q, K, V and O must be bfloat16")
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+
+
+@dataclass
+class Mask:
+    """The mask menu of attn_mask_desc (AND-composed).
+
+    causal: k <= p;  window=(left, right): p-left <= k <= p+right (negative =
+    unbounded side);  block_size: block-diffusion k < bs*(p//bs + 1);
+    doc_offsets: int32 [B, num_docs+1] cumulative document starts on the GPU.
+    """
+    causal: bool = False
+    window: tuple | None = None
+    block_size: int | None = None
+    doc_offsets: torch.Tensor | None = None
+
+    def desc(self) -> attn_mask_desc:
+        d = attn_mask_desc()
+        d.flags = 0
+        d.window_left = d.window_right = -1
+        d.block_size = 0
+        d.doc_offsets = None
+        d.num_docs = 0
+        d.doc_stride = 0
+        if self.causal:
+            d.flags |= MASK_CAUSAL
+        if self.window is not None:
+            d.flags |= MASK_WINDOW
+            d.window_left, d.window_right = int(self.window[0]), int(self.window[1])
+        if self.block_size is not None:
+            d.flags |= MASK_BLOCK_CAUSAL
+            d.block_size = int(self.block_size)
+        if self.doc_offsets is not None:
+            off = self.doc_offsets
+            if off.dtype != torch.int32 or off.dim() != 2 or off.stride(1) != 1:
+                raise TypeError("doc_offsets must be int32 [B, num_docs+1] with rows contiguous")
+            d.flags |= MASK_DOCUMENT
+            d.doc_offsets = off.data_ptr()
+            d.num_docs = off.shape[1] - 1
+            d.doc_stride = off.stride(0)
+        return d
+
+
+def _mask_ptr(mask):
+    if mask is None:
+        return None, None
+    d = mask.desc() if isinstance(mask, Mask) else mask
+    return d, ctypes.byref(d)
+
+
+def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None):
+    """O (and LSE) for q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] bf16 CUDA tensors (any B/H/N strides)."""
+    _bf16(q, k, v, o)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    st = _lib.attn_fwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                       _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, scale, mp,
+                       _stream(stream))
+    _check("attn_fwd", st)
+    return o, lse
+
+
+class BlockMask:
+    """Device buffers of one attn_blockmask (allocated with torch on ``device``)."""
+
+    def __init__(self, Bm, Hm, Nq, Nk, device="cuda"):
+        self.Bm, self.Hm = Bm, Hm
+        self.nQt = (Nq + BLOCKMASK_TILE - 1) // BLOCKMASK_TILE
+        self.nKt = (Nk + BLOCKMASK_TILE - 1) // BLOCKMASK_TILE
+        i32 = dict(dtype=torch.int32, device=device)
+        self.part_num = torch.zeros(Bm, Hm, self.nQt, **i32)
+        self.full_num = torch.zeros(Bm, Hm, self.nQt, **i32)
+        self.part_idx = torch.zeros(Bm, Hm, self.nQt, max(self.nKt, 1), **i32)
+        self.full_idx = torch.zeros(Bm, Hm, self.nQt, max(self.nKt, 1), **i32)
+
+    def struct(self) -> attn_blockmask:
+        s = attn_blockmask()
+        s.Bm, s.Hm, s.nQt, s.nKt = self.Bm, self.Hm, self.nQt, self.nKt
+        s.part_num, s.part_idx = self.part_num.data_ptr(), self.part_idx.data_ptr()
+        s.full_num, s.full_idx = self.full_num.data_ptr(), self.full_idx.data_ptr()
+        return s
+
+
+def attn_blockmask_bytes(Bm, Hm, nQt, nKt):
+    return int(_lib.attn_blockmask_bytes(Bm, Hm, nQt, nKt))
+
+
+def attn_build_blockmask(bm: BlockMask, B, Nq, Nk, mask=None, tile_map=None, stream=None):
+    """Fill ``bm`` from a uint8 tile map [Bm, Hm, nQt, nKt] (CUDA) or from ``mask``."""
+    if tile_map is not None and (tile_map.dtype != torch.uint8 or not tile_map.is_contiguous()):
+        raise TypeError("tile_map must be a contiguous uint8 tensor")
+    keep, mp = _mask_ptr(mask)
+    s = bm.struct()
+    st = _lib.attn_build_blockmask(mp, _ptr(tile_map), B, Nq, Nk, ctypes.byref(s), _stream(stream))
+    _check("attn_build_blockmask", st)
+    return bm
+
+
+def attn_fwd_blockmask(q, k, v, o, bm: BlockMask, lse=None, scale=None, mask=None, stream=None):
+    _bf16(q, k, v, o)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    s = bm.struct()
+    st = _lib.attn_fwd_blockmask(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                 _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, scale,
+                                 mp, ctypes.byref(s), _stream(stream))
+    _check("attn_fwd_blockmask", st)
+    return o, lse
+
+
+def attn_decode_num_splits(B, Hkv, max_pages, num_cus=None):
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return int(_lib.attn_decode_num_splits(B, Hkv, max_pages, num_cus))
+
+
+def attn_decode_ws_o_bytes(B, Hq, Lq, D, S):
+    return int(_lib.attn_decode_ws_o_bytes(B, Hq, Lq, D, S))
+
+
+def attn_decode_ws_lse_bytes(B, Hq, Lq, S):
+    return int(_lib.attn_decode_ws_lse_bytes(B, Hq, Lq, S))
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, num_splits,
+                        ws_o, ws_lse, scale=None, mask=None, stream=None):
+    """Split-KV partials: q [B,Hq,Lq,D]; caches [pages, page_size, Hkv, D] (contiguous);
+    block_table int32 [B, >=max_pages]; seq_lens int32 [B]; ws_o float [B,Hq,Lq,S,D];
+    ws_lse float [B,Hq,Lq,S]."""
+    _bf16(q)
+    if k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("KV caches must be bfloat16")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("KV caches must be contiguous [pages, page_size, Hkv, D]")
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("K and V caches differ in shape")
+    if block_table.dtype != torch.int32 or block_table.stride(1) != 1:
+        raise TypeError("block_table must be int32 with contiguous rows")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be contiguous int32")
+    if ws_o.dtype != torch.float32 or ws_lse.dtype != torch.float32:
+        raise TypeError("workspaces must be float32")
+    B, Hq, Lq, D = q.shape
+    n_pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head dim mismatch")
+    if ws_o.numel() * 4 < attn_decode_ws_o_bytes(B, Hq, Lq, D, num_splits) or \
+            ws_lse.numel() * 4 < attn_decode_ws_lse_bytes(B, Hq, Lq, num_splits):
+        raise ValueError("workspace too small")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    st = _lib.attn_decode_splitkv(_ptr(q), _strides(q), _ptr(k_cache), _ptr(v_cache), n_pages,
+                                  _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                                  int(max_pages), B, Hq, Hkv, Lq, D, page_size, int(num_splits),
+                                  scale, mp, _ptr(ws_o), _ptr(ws_lse), _stream(stream))
+    _check("attn_decode_splitkv", st)
+    return ws_o, ws_lse
+
+
+def attn_decode_combine(ws_o, ws_lse, o, lse=None, stream=None):
+    """O [B,Hq,Lq,D] bf16 (and LSE [B,Hq,Lq]) from ws_o [B,Hq,Lq,S,D], ws_lse [B,Hq,Lq,S]."""
+    _bf16(o)
+    B, Hq, Lq, S, D = ws_o.shape
+    if ws_o.dtype != torch.float32 or not ws_o.is_contiguous() or not ws_lse.is_contiguous():
+        raise TypeError("workspaces must be contiguous float32")
+    st = _lib.attn_decode_combine(_ptr(ws_o), _ptr(ws_lse), B, Hq, Lq, S, D, _ptr(o), _strides(o),
+                                  _ptr(lse), _stream(stream))
+    _check("attn_decode_combine", st)
+    return o, lse
+
+
+def attn_status_str(status: int) -> str:
+    return _lib.attn_status_str(status).decode()
+
+
+def attn_abi_version() -> int:
+    return int(_lib.attn_abi_version())
+
+
+def lib_handle():
+    """The loaded ctypes library (for direct C-ABI calls in tests)."""
+    return _lib

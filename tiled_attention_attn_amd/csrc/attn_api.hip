@@ -1,0 +1,287 @@
+// C ABI of the attention library: argument validation, launch geometry and
+// status codes.  Everything here runs on the host; the work itself is in the
+// kernels of fwd.hip, blockmask.hip and decode.hip.  Nothing is allocated,
+// freed or synchronised here (see include/tiled_attn.h for the contract).
+#include <cmath>
+#include <cstdint>
+
+#include "params.h"
+
+namespace tattn {
+int launch_fwd(const FwdParams& p, int D, bool blockmask, hipStream_t stream);
+int launch_blockmask(const BmBuildParams& p, hipStream_t stream);
+int launch_decode(const DecParams& p, int D, hipStream_t stream);
+int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
+                   bf16* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
+                   hipStream_t stream);
+}  // namespace tattn
+
+using namespace tattn;
+
+namespace {
+
+constexpr int kMaxLen = 1 << 28;  // keeps every key / row index and product in range
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_strides(const int64_t s[3]) {
+  if (s == nullptr) return ATTN_ERR_NULL;
+  for (int i = 0; i < 3; ++i)
+    if (s[i] < 0 || (s[i] & 7) != 0) return ATTN_ERR_STRIDE;
+  return ATTN_OK;
+}
+
+int check_scale(float scale) {
+  return (std::isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
+}
+
+// Converts the public mask descriptor; `allow_doc` is false for decode.
+int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParams& out) {
+  out = MaskParams{0u, -1, -1, 1, nullptr, 1, 2};
+  if (m == nullptr) return ATTN_OK;
+  if (m->flags & ~ATTN_MASK_ALL) return ATTN_ERR_MASK;
+  out.flags = m->flags;
+  out.wl = m->window_left < 0 ? -1 : m->window_left;
+  out.wr = m->window_right < 0 ? -1 : m->window_right;
+  if (m->flags & ATTN_MASK_BLOCK_CAUSAL) {
+    if (m->block_size <= 0) return ATTN_ERR_MASK;
+    out.bs = m->block_size;
+  }
+  if (m->flags & ATTN_MASK_DOCUMENT) {
+    if (!allow_doc) return ATTN_ERR_MASK;
+    if (m->doc_offsets == nullptr) return ATTN_ERR_NULL;
+    if (m->num_docs < 1 || m->doc_stride < m->num_docs + 1) return ATTN_ERR_MASK;
+    if (Nq > Nk) return ATTN_ERR_MASK;
+    out.doc = m->doc_offsets;
+    out.num_docs = m->num_docs;
+    out.doc_stride = m->doc_stride;
+  }
+  return ATTN_OK;
+}
+
+int check_common(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                 const void* v, const int64_t* vs, const void* o, const int64_t* os, int B,
+                 int Hq, int Hkv, int Nq, int Nk, int D, float scale) {
+  // K and V may be NULL when there are no keys (an empty tensor has no storage).
+  if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_NULL;
+  int st;
+  if ((st = check_strides(qs)) || (st = check_strides(ks)) || (st = check_strides(vs)) ||
+      (st = check_strides(os)))
+    return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
+    return ATTN_ERR_ALIGN;
+  return check_scale(scale);
+}
+
+void fill_fwd(FwdParams& p, const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+              const void* v, const int64_t* vs, void* o, const int64_t* os, float* lse, int B,
+              int Hq, int Hkv, int Nq, int Nk, float scale) {
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.v = static_cast<const bf16*>(v);
+  p.o = static_cast<bf16*>(o);
+  p.lse = lse;
+  p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sn = qs[2];
+  p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sn = ks[2];
+  p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sn = vs[2];
+  p.o_sb = os[0]; p.o_sh = os[1]; p.o_sn = os[2];
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.c2 = scale * 1.4426950408889634f;
+  p.n_qt = (Nq + 127) / 128;
+  p.part_num = p.part_idx = p.full_num = p.full_idx = nullptr;
+  p.bm_B = p.bm_H = 1;
+  p.nKt = (Nk + 127) / 128;
+}
+
+void set_slots(FwdParams& p, bool paired) {
+  p.paired = paired && p.n_qt > 1;
+  p.n_slots = p.paired ? (p.n_qt + 1) / 2 : p.n_qt;
+  const long units = (long)p.B * p.Hq * p.n_slots;
+  p.xcd_remap = (units % 8) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "a size is negative or over its limit";
+    case ATTN_ERR_HEAD_DIM: return "head dim D must be 64 or 128";
+    case ATTN_ERR_GQA: return "Hq must be a positive multiple of Hkv";
+    case ATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements";
+    case ATTN_ERR_ALIGN: return "tensor base pointers must be 16-byte aligned";
+    case ATTN_ERR_MASK: return "unknown mask flag or bad mask parameter";
+    case ATTN_ERR_WORKSPACE: return "workspace or split arguments inconsistent";
+    case ATTN_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    case ATTN_ERR_BLOCKMASK: return "BlockMask descriptor inconsistent with the shapes";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+             const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3],
+             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             const attn_mask_desc* mask, hipStream_t stream) {
+  int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
+                        D, scale);
+  if (st) return st;
+  FwdParams p;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
+  // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
+  set_slots(p, (p.mask.flags & (ATTN_MASK_CAUSAL | ATTN_MASK_BLOCK_CAUSAL)) != 0 &&
+                   !(p.mask.flags & (ATTN_MASK_WINDOW | ATTN_MASK_DOCUMENT)));
+  return launch_fwd(p, D, false, stream);
+}
+
+size_t attn_blockmask_bytes(int Bm, int Hm, int nQt, int nKt) {
+  if (Bm <= 0 || Hm <= 0 || nQt < 0 || nKt < 0) return 0;
+  const size_t rows = (size_t)Bm * Hm * nQt;
+  return rows * 4 * 2 + rows * (size_t)nKt * 4 * 2;
+}
+
+int attn_build_blockmask(const attn_mask_desc* mask, const uint8_t* tile_map, int B, int Nq,
+                         int Nk, attn_blockmask* out, hipStream_t stream) {
+  if (out == nullptr) return ATTN_ERR_NULL;
+  if (!out->part_num || !out->part_idx || !out->full_num || !out->full_idx) return ATTN_ERR_NULL;
+  if (Nq < 0 || Nk < 0 || Nq > kMaxLen || Nk > kMaxLen) return ATTN_ERR_SHAPE;
+  if (out->Bm < 1 || out->Hm < 1 || out->Bm > 65535 || out->Hm > 65535) return ATTN_ERR_BLOCKMASK;
+  if (out->nQt != (Nq + 127) / 128 || out->nKt != (Nk + 127) / 128) return ATTN_ERR_BLOCKMASK;
+  BmBuildParams p;
+  int st = make_mask(mask, Nq, Nk, true, p.mask);
+  if (st) return st;
+  if (tile_map == nullptr) {
+    if (mask == nullptr) return ATTN_ERR_NULL;
+    if ((p.mask.flags & ATTN_MASK_DOCUMENT) && out->Bm != B) return ATTN_ERR_BLOCKMASK;
+  }
+  if (out->nQt == 0) return ATTN_OK;
+  p.tile_map = tile_map;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.shift = (int64_t)Nk - Nq;
+  p.Bm = out->Bm; p.Hm = out->Hm; p.nQt = out->nQt; p.nKt = out->nKt;
+  p.part_num = out->part_num; p.part_idx = out->part_idx;
+  p.full_num = out->full_num; p.full_idx = out->full_idx;
+  return launch_blockmask(p, stream);
+}
+
+int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
+                       const int64_t k_stride[3], const void* v, const int64_t v_stride[3],
+                       void* o, const int64_t o_stride[3], float* lse, int B, int Hq, int Hkv,
+                       int Nq, int Nk, int D, float scale, const attn_mask_desc* mask,
+                       const attn_blockmask* bm, hipStream_t stream) {
+  int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
+                        D, scale);
+  if (st) return st;
+  if (bm == nullptr) return ATTN_ERR_NULL;
+  if (!bm->part_num || !bm->part_idx || !bm->full_num || !bm->full_idx) return ATTN_ERR_NULL;
+  if (bm->nQt != (Nq + 127) / 128 || bm->nKt != (Nk + 127) / 128) return ATTN_ERR_BLOCKMASK;
+  if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
+  FwdParams p;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
+  p.part_num = bm->part_num; p.part_idx = bm->part_idx;
+  p.full_num = bm->full_num; p.full_idx = bm->full_idx;
+  p.bm_B = bm->Bm; p.bm_H = bm->Hm;
+  set_slots(p, true);
+  return launch_fwd(p, D, true, stream);
+}
+
+size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits) {
+  if (B < 0 || Hq < 0 || Lq < 0 || D <= 0 || num_splits <= 0) return 0;
+  return (size_t)B * Hq * Lq * num_splits * D * sizeof(float);
+}
+
+size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits) {
+  if (B < 0 || Hq < 0 || Lq < 0 || num_splits <= 0) return 0;
+  return (size_t)B * Hq * Lq * num_splits * sizeof(float);
+}
+
+int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
+  if (B <= 0 || Hkv <= 0 || max_pages <= 0) return 1;
+  if (num_cus <= 0) num_cus = 256;
+  // Two resident work groups per compute unit; round the work-group count up
+  // to a whole number of waves of the machine.
+  const long units = (long)B * Hkv;
+  const long target = 2L * num_cus;
+  long s = (target + units - 1) / units;
+  if (s < 1) s = 1;
+  if (s > max_pages) s = max_pages;
+  return (int)s;
+}
+
+int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_cache,
+                        const void* v_cache, int64_t num_pages, const int32_t* block_table,
+                        int64_t bt_stride, const int32_t* seq_lens, int max_pages, int B, int Hq,
+                        int Hkv, int Lq, int D, int page_size, int num_splits, float scale,
+                        const attn_mask_desc* mask, float* ws_o, float* ws_lse,
+                        hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !ws_o || !ws_lse)
+    return ATTN_ERR_NULL;
+  int st = check_strides(q_stride);
+  if (st) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Lq < 0 || num_pages < 1 || page_size < 1 || max_pages < 1)
+    return ATTN_ERR_SHAPE;
+  if (B > 65535 || Hkv > 65535 || Lq > 65536) return ATTN_ERR_SHAPE;
+  if ((int64_t)max_pages * page_size > kMaxLen) return ATTN_ERR_SHAPE;
+  if (bt_stride < max_pages) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws_o))
+    return ATTN_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  if (num_splits < 1 || num_splits > 65536) return ATTN_ERR_WORKSPACE;
+  DecParams p;
+  attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
+  if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
+  if (B == 0 || Lq == 0) return ATTN_OK;
+  const int G = Hq / Hkv;
+  p.q = static_cast<const bf16*>(q);
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.kc = static_cast<const bf16*>(k_cache);
+  p.vc = static_cast<const bf16*>(v_cache);
+  p.bt = block_table;
+  p.bt_stride = bt_stride;
+  p.seq_lens = seq_lens;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.Lq = Lq; p.ps = page_size; p.S = num_splits;
+  p.chunk = page_size * ((max_pages + num_splits - 1) / num_splits);
+  p.max_keys = max_pages * page_size;
+  p.num_pages = num_pages;
+  p.rows = G * Lq;
+  p.n_rg = (p.rows + 63) / 64;
+  if ((long)p.S * p.n_rg > 0x7fffffffL) return ATTN_ERR_SHAPE;
+  p.c2 = scale * 1.4426950408889634f;
+  p.ws_o = ws_o;
+  p.ws_lse = ws_lse;
+  return launch_decode(p, D, stream);
+}
+
+int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S,
+                        int D, void* o, const int64_t o_stride[3], float* lse,
+                        hipStream_t stream) {
+  if (!ws_o || !ws_lse || !o) return ATTN_ERR_NULL;
+  int st = check_strides(o_stride);
+  if (st) return st;
+  if (B < 0 || Hq < 0 || Lq < 0) return ATTN_ERR_SHAPE;
+  if ((long)B * Hq * Lq > 0x7fffffffL) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (S < 1 || S > 65536) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(o)) return ATTN_ERR_ALIGN;
+  if (B == 0 || Hq == 0 || Lq == 0) return ATTN_OK;
+  return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, static_cast<bf16*>(o), o_stride[0],
+                        o_stride[1], o_stride[2], lse, stream);
+}
+
+}  // extern "C"

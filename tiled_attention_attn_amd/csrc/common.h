@@ -1,0 +1,140 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// and LDS-transpose wrappers, cross-half exchanges, bf16 packing and the
+// per-row mask interval.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tiled_attn.h"
+
+namespace tattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+#define TATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---- MFMA ------------------------------------------------------------------
+// 32x32x16 bf16: lane l holds A[m=l%32][k=8(l/32)+i], B[k=8(l/32)+i][n=l%32],
+// C[m=8(r/4)+4(l/32)+r%4][n=l%32].  16x16x32 bf16: A[m=l%16][k=8(l/16)+i],
+// B[k=8(l/16)+i][n=l%16], C[m=4(l/16)+r][n=l%16].  (Checked on gfx950 with an
+// in-bounds probe of every lane and slot.)
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- LDS access --------------------------------------------------------------
+__device__ __forceinline__ bf16x8 lds_read_b128(const TATTN_LDS char* base, uint32_t byte_off) {
+  return *reinterpret_cast<const TATTN_LDS bf16x8*>(base + byte_off);
+}
+
+// ds_read_b64_tr_b16.  Within each 16-lane group, lane j reads 4 halfwords
+// (row j of a 16x4 matrix M); lane i receives (M[i/4][i%4], M[4+i/4][i%4],
+// M[8+i/4][i%4], M[12+i/4][i%4]).  So when lane j reads 8 bytes at
+// row (base + j/4), columns (c0 + 4(j%4)) .. +3 of a row-major matrix, lane i
+// receives column c0 + i of rows base .. base+3: a transposed 4-element load.
+__device__ __forceinline__ i16x4 lds_read_tr16(const TATTN_LDS char* base, uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<TATTN_LDS i16x4*>(const_cast<TATTN_LDS char*>(base) + byte_off));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's
+// 16 bytes land at lds_wave_base + 16 * l.  lds_wave_base must be uniform.
+__device__ __forceinline__ void dma16(const void* gsrc, TATTN_LDS void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+
+// ---- cross-lane ----------------------------------------------------------------
+// Value of the lane 32 positions away (lanes l and l^32 exchange).
+__device__ __forceinline__ float other_half(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lane = __lane_id();
+  return __builtin_bit_cast(float, lane < 32 ? (uint32_t)r[1] : (uint32_t)r[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// fp32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);
+}
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                        float a5, float a6, float a7) {
+  bf16x2 p0 = pack2(a0, a1), p1 = pack2(a2, a3), p2 = pack2(a4, a5), p3 = pack2(a6, a7);
+  bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+// ---- mask ----------------------------------------------------------------------
+struct MaskParams {
+  uint32_t flags;
+  int32_t wl, wr, bs;
+  const int32_t* doc;
+  int32_t num_docs, doc_stride;
+};
+
+__device__ __forceinline__ int64_t floordiv(int64_t a, int64_t b) {
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Visible keys of the row at absolute position p: [lo, hi] (empty when lo > hi).
+// Every flag gives an interval whose ends never decrease with p, and the
+// clamping to [0, Nk-1] keeps that property, so over a block of consecutive
+// rows the first row has the smallest lo and the last row the largest hi.
+__device__ __forceinline__ void row_interval(const MaskParams& m, int b, int64_t p, int Nk,
+                                             int& lo_out, int& hi_out) {
+  int64_t lo = 0, hi = (int64_t)Nk - 1;
+  if (m.flags & ATTN_MASK_CAUSAL) hi = hi < p ? hi : p;
+  if (m.flags & ATTN_MASK_WINDOW) {
+    if (m.wl >= 0) { int64_t a = p - m.wl; lo = lo > a ? lo : a; }
+    if (m.wr >= 0) { int64_t a = p + m.wr; hi = hi < a ? hi : a; }
+  }
+  if (m.flags & ATTN_MASK_BLOCK_CAUSAL) {
+    int64_t a = (floordiv(p, m.bs) + 1) * m.bs - 1;
+    hi = hi < a ? hi : a;
+  }
+  if ((m.flags & ATTN_MASK_DOCUMENT) && Nk > 0) {
+    const int32_t* off = m.doc + (int64_t)b * m.doc_stride;
+    int64_t pc = p < 0 ? 0 : (p >= Nk ? Nk - 1 : p);
+    // largest d in [0, num_docs) with off[d] <= pc
+    int lo_d = 0, hi_d = m.num_docs - 1;
+    while (lo_d < hi_d) {
+      int mid = (lo_d + hi_d + 1) >> 1;
+      if (off[mid] <= pc) lo_d = mid; else hi_d = mid - 1;
+    }
+    int64_t s = off[lo_d], e = (int64_t)off[lo_d + 1] - 1;
+    lo = lo > s ? lo : s;
+    hi = hi < e ? hi : e;
+  }
+  if (lo < 0) lo = 0;
+  if (hi > (int64_t)Nk - 1) hi = (int64_t)Nk - 1;
+  lo_out = (int)lo;
+  hi_out = (int)hi;
+}
+
+}  // namespace tattn

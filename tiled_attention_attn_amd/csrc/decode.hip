@@ -1,0 +1,292 @@
+// Split-KV paged decode and the log-sum-exp combine for gfx950.
+//
+// "Short query + long KV": the FlexAttention / DFlash article (section 1)
+// names FlashDecoding-style split-KV decoding with GQA over a paged KV cache
+// addressed through a block table.  Each work group here owns one
+// (sequence, KV head, key split) and all the query rows that read that KV
+// head -- G query heads x Lq draft tokens, packed 16 rows per wave -- so
+// every K/V byte of the split is read from HBM exactly once.  Within the
+// split the keys stream through LDS in 64-key steps with the same online
+// softmax as the prefill (running max, exp-sum, rescaled accumulator), and
+// the split's normalised partial O_s and LSE_s go to an fp32 workspace.  The
+// combine kernel then merges the splits by their LSE.
+//
+// gfx950 mapping:
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
+//    16 query rows per block); the S^T registers are the P^T operand
+//    directly, and V^T comes from LDS through ds_read_b64_tr_b16.
+//  * Page rows (256 bytes at D=128) are copied global -> LDS with
+//    global_load_lds_dwordx4, double-buffered; block-table entries for the
+//    next step are loaded a step ahead so no load waits on another.
+#include "params.h"
+
+namespace tattn {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecKBlk = 64;
+
+template <int D> struct DSwz;
+template <> struct DSwz<64> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r >> 2) ^ (r << 1)) & 7u; }
+};
+template <> struct DSwz<128> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r ^ (r << 2)) & 15u; }
+};
+template <int D>
+__device__ __forceinline__ uint32_t dtile_off(uint32_t row, uint32_t chunk) {
+  return row * (2 * D) + 16u * (chunk ^ DSwz<D>::f(row));
+}
+
+__device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
+
+template <int D>
+__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_kernel(const DecParams p) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per key row
+  constexpr int INSTS = kDecKBlk * CPR / 64;       // wave instructions per tile
+  constexpr int PER_WAVE = INSTS / (kDecThreads / 64);
+  constexpr int TILE_BYTES = kDecKBlk * D * 2;
+  constexpr int NC = D / 32;   // d-chunks of the QK MFMA (K = 32)
+  constexpr int NDB = D / 16;  // d-blocks of the PV MFMA (M = 16)
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_BYTES];
+  TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
+  TATTN_LDS char* bufK[2] = {smem, smem + 2 * TILE_BYTES};
+  TATTN_LDS char* bufV[2] = {smem + TILE_BYTES, smem + 3 * TILE_BYTES};
+
+  const int s = blockIdx.x % p.S, rg = blockIdx.x / p.S;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 4, col = lane & 15;
+
+  // Sequence length as given, clamped to what the block table can address.
+  const int seq_len = min(max(p.seq_lens[b], 0), p.max_keys);
+  const int k_begin = s * p.chunk;
+  const int k_end = min(seq_len, k_begin + p.chunk);
+
+  // This lane's query row (the N index of its MFMA column).
+  const int rr = rg * 64 + wave * 16 + col;
+  const bool row_ok = rr < p.rows;
+  const int rrc = row_ok ? rr : p.rows - 1;
+  const int g = rrc / p.Lq, t = rrc % p.Lq;
+  const int hq = kvh * p.G + g;
+  const int64_t pos = (int64_t)seq_len - p.Lq + t;
+  int lo = 1, hi = 0;
+  if (seq_len > 0) row_interval(p.mask, b, pos, seq_len, lo, hi);
+  lo = max(lo, k_begin);
+  hi = min(hi, k_end - 1);
+  if (!row_ok) { lo = 1; hi = 0; }
+
+  // Keys any row of this group can see: rows differ only in t, and the
+  // interval ends never decrease with t, so t = 0 and t = Lq-1 bound them.
+  int klo = k_end, khi = k_begin - 1;
+  if (seq_len > 0 && k_end > k_begin) {
+    int a0, a1, c0, c1;
+    row_interval(p.mask, b, (int64_t)seq_len - p.Lq, seq_len, a0, a1);
+    row_interval(p.mask, b, (int64_t)seq_len - 1, seq_len, c0, c1);
+    klo = max(a0, k_begin);
+    khi = min(c1, k_end - 1);
+  }
+  int n_steps = 0, kb0 = k_begin;
+  if (khi >= klo) {
+    kb0 = k_begin + ((klo - k_begin) / kDecKBlk) * kDecKBlk;
+    n_steps = (khi + 1 - kb0 + kDecKBlk - 1) / kDecKBlk;
+  }
+  // Rows of this wave that are unmasked on a whole step: bounds over the wave.
+  int wlo = row_ok ? lo : -0x3fffffff, whi = row_ok ? hi : 0x3fffffff;
+  for (int m = 32; m >= 1; m >>= 1) {
+    wlo = max(wlo, __shfl_xor(wlo, m, 64));
+    whi = min(whi, __shfl_xor(whi, m, 64));
+  }
+
+  // Q^T fragments (B operand, k = head dim, n = row).
+  bf16x8 qf[NC];
+  {
+    const bf16* src = p.q + b * p.q_sb + hq * p.q_sh + (int64_t)t * p.q_sn + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 32 * c);
+  }
+
+  const int32_t* bt_row = p.bt + b * p.bt_stride;
+  const int64_t row_stride = (int64_t)p.Hkv * D;  // elements between slots of a page
+  // Pages of the key rows this lane copies in a step.
+  int pg[PER_WAVE];
+  auto load_pages = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      int key = kb + ((wave * PER_WAVE + i) * 64 + lane) / CPR;
+      key = key < seq_len ? key : seq_len - 1;
+      const int page = bt_row[key / p.ps];
+      pg[i] = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+    }
+  };
+  auto issue = [&](int kb, int buf) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int inst = wave * PER_WAVE + i;
+      const int slot = inst * 64 + lane;
+      const uint32_t row = slot / CPR;
+      const uint32_t chunk = (slot % CPR) ^ DSwz<D>::f(row);
+      int key = kb + (int)row;
+      key = key < seq_len ? key : seq_len - 1;
+      const int64_t off = ((int64_t)pg[i] * p.ps + key % p.ps) * row_stride + kvh * D + chunk * 8;
+      dma16(p.kc + off, bufK[buf] + inst * 1024);
+      dma16(p.vc + off, bufV[buf] + inst * 1024);
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) oacc[d] = f32x4{};
+
+  if (n_steps > 0) {
+    load_pages(kb0);
+    wait_vmem();
+    issue(kb0, 0);
+    if (n_steps > 1) load_pages(kb0 + kDecKBlk);
+  }
+  for (int st = 0; st < n_steps; ++st) {
+    const int kb = kb0 + st * kDecKBlk;
+    wait_vmem();
+    __syncthreads();
+    if (st + 1 < n_steps) {
+      issue(kb + kDecKBlk, (st + 1) & 1);
+      if (st + 2 < n_steps) load_pages(kb + 2 * kDecKBlk);
+    }
+    const TATTN_LDS char* tK = bufK[st & 1];
+    const TATTN_LDS char* tV = bufV[st & 1];
+
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb16 = 0; kb16 < 4; ++kb16) {
+      sacc[kb16] = f32x4{};
+      const uint32_t row = 16 * kb16 + col;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sacc[kb16] = mfma16(lds_read_b128(tK, dtile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
+    }
+    const bool full = kb >= wlo && kb + kDecKBlk - 1 <= whi;
+    if (!full) {
+#pragma unroll
+      for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 16 * kb16 + 4 * grp + r;
+          if (key < lo || key > hi) sacc[kb16][r] = kNegInf;
+        }
+    }
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int kb16 = 0; kb16 < 4; ++kb16)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb16][r]);
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float m_new = fmaxf(m_run, mx * p.c2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = fast_exp2(__builtin_fmaf(sacc[2 * kc + (i >> 2)][i & 3], p.c2, -m_use));
+        l_run += e[i];
+      }
+      pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const uint32_t r1 = 32 * kc + 4 * grp + (col >> 2);
+      const uint32_t r2 = r1 + 16;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t dcol = 16 * db + 4 * (col & 3);
+        const uint32_t sub = 8 * (col & 1);
+        const i16x4 v0 = lds_read_tr16(tV, dtile_off<D>(r1, dcol >> 3) + sub);
+        const i16x4 v1 = lds_read_tr16(tV, dtile_off<D>(r2, dcol >> 3) + sub);
+        oacc[db] = mfma16(join_tr(v0, v1), pf[kc], oacc[db]);
+      }
+    }
+  }
+
+  // Partial result of this split: normalised O_s and LSE_s.
+  float l_tot = l_run + xor_lane(l_run, 16);
+  l_tot += xor_lane(l_tot, 32);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int64_t orow = (((int64_t)b * p.Hq + hq) * p.Lq + t) * p.S + s;
+    float* dst = p.ws_o + orow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f32x4 w = oacc[db] * inv;
+      *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * grp) = w;
+    }
+    if (grp == 0) p.ws_lse[orow] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  }
+}
+
+// One wave per (sequence, head, query) row: LSE = log sum_s exp(LSE_s),
+// O = sum_s exp(LSE_s - LSE) O_s.
+template <int D>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ ws_o,
+                                                      const float* __restrict__ ws_lse,
+                                                      int n_rows, int Hq, int Lq, int S,
+                                                      bf16* o, int64_t o_sb, int64_t o_sh,
+                                                      int64_t o_sn, float* lse) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= n_rows) return;
+  const float* L = ws_lse + (int64_t)row * S;
+  float m = kNegInf;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, L[s]);
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+  const float m_use = m == kNegInf ? 0.f : m;
+  float tot = 0.f;
+  for (int s = lane; s < S; s += 64) tot += __expf(L[s] - m_use);
+  for (int k = 32; k >= 1; k >>= 1) tot += __shfl_xor(tot, k, 64);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  const float* O = ws_o + (int64_t)row * S * D;
+  for (int s = 0; s < S; ++s) {
+    const float w = __expf(L[s] - m_use) * inv;  // L[s] = -inf gives 0
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += w * O[(int64_t)s * D + lane + 64 * i];
+  }
+  const int t = row % Lq, bh = row / Lq, h = bh % Hq, b = bh / Hq;
+  bf16* dst = o + b * o_sb + h * o_sh + (int64_t)t * o_sn;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) dst[lane + 64 * i] = (bf16)acc[i];
+  if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m_use + logf(tot) : kNegInf;
+}
+
+int launch_decode(const DecParams& p, int D, hipStream_t stream) {
+  dim3 grid(p.S * p.n_rg, p.Hkv, p.B), block(kDecThreads);
+  if (D == 64) hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
+                   bf16* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
+                   hipStream_t stream) {
+  const int n_rows = B * Hq * Lq;
+  dim3 grid((n_rows + 3) / 4), block(256);
+  if (D == 64)
+    hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq, Lq,
+                       S, o, o_sb, o_sh, o_sn, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq, Lq,
+                       S, o, o_sb, o_sh, o_sn, lse);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace tattn

@@ -1,0 +1,301 @@
+// Prefill: fused, IO-aware exact attention for gfx950.
+//
+// One work group of 4 waves owns a 128-row query tile (32 rows per wave) and
+// streams the visible keys through LDS in 64-key steps, as the tiled method
+// of "FlashAttention 2 principles and PyTorch practice" (sections 1 and 3.1)
+// describes: the Q block stays on chip, K/V blocks are loaded once per step,
+// and an online softmax (section 3.2: running max M and exp-sum L, the
+// accumulator rescaled whenever M moves) means scores and probabilities
+// never reach HBM.  Mask variants follow the FlexAttention / DFlash article:
+// per-row intervals for the dense masks (section 1 mask_mod, section 3's
+// symmetric window) and explicit FULL / PARTIAL tile lists for BlockMask.
+//
+// gfx950 mapping:
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the M dimension,
+//    queries the N dimension), so each lane owns one query column and the row
+//    max / row sum are in-lane except for one exchange with lane l^32
+//    (v_permlane32_swap).
+//  * The S^T accumulator registers, converted to bf16, are directly the
+//    B operand of O^T += V^T P^T: the order of the 16 keys inside each PV
+//    MFMA is permuted the same way on the V side, which needs no shuffle.
+//  * V^T operands come from LDS with ds_read_b64_tr_b16 (transposing loads);
+//    K operands with ds_read_b128.  Both tiles use an XOR swizzle of 16-byte
+//    chunks that keeps these reads free of bank conflicts.
+//  * K/V tiles are copied global -> LDS by global_load_lds_dwordx4 (no
+//    registers), double-buffered: step j+1 is in flight while step j computes.
+//  * Causal-like masks pair query tile i with tile n-1-i in one work group so
+//    every group does the same amount of work; the group -> (batch, head)
+//    mapping keeps all tiles of a head (and of a GQA group) on one XCD so its
+//    K/V stay in that XCD's L2.
+#include "params.h"
+
+namespace tattn {
+
+constexpr int kQTile = 128;
+constexpr int kKBlk = 64;
+constexpr int kThreads = 256;
+
+// XOR swizzle of the 16-byte chunks of tile row r (see the header comment).
+template <int D> struct Swz;
+template <> struct Swz<64> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r >> 2) ^ (r << 1)) & 7u; }
+};
+template <> struct Swz<128> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r ^ (r << 2)) & 15u; }
+};
+
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
+  return row * (2 * D) + 16u * (chunk ^ Swz<D>::f(row));
+}
+
+struct Step {
+  int kb;      // first key of the step
+  int masked;  // apply [lo_m, hi_m] per element
+  int use_row_interval;  // 1: the row's own mask interval; 0: only k < Nk
+};
+
+template <int D>
+__device__ __forceinline__ void issue_tile_loads(const bf16* __restrict__ Kbh,
+                                                 const bf16* __restrict__ Vbh, int64_t k_sn,
+                                                 int64_t v_sn, int kb, int Nk,
+                                                 TATTN_LDS char* ldsK, TATTN_LDS char* ldsV,
+                                                 int wave, int lane) {
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int INSTS = kKBlk * CPR / 64;         // wave instructions per tile
+  constexpr int PER_WAVE = INSTS / (kThreads / 64);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;
+    const int slot = inst * 64 + lane;
+    const uint32_t row = slot / CPR;
+    const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
+    int key = kb + (int)row;
+    key = key < Nk ? key : Nk - 1;
+    dma16(Kbh + (int64_t)key * k_sn + chunk * 8, ldsK + inst * 1024);
+    dma16(Vbh + (int64_t)key * v_sn + chunk * 8, ldsV + inst * 1024);
+  }
+}
+
+template <int D, bool BM>
+__device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
+                                             int b, int h, int kvh) {
+  constexpr int TILE_BYTES = kKBlk * D * 2;
+  constexpr int NC = D / 16;   // d-chunks of the QK MFMA
+  constexpr int NDB = D / 32;  // d-blocks of the PV MFMA
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5;
+
+  const bf16* __restrict__ Qbh = p.q + b * p.q_sb + h * p.q_sh;
+  const bf16* __restrict__ Kbh = p.k + b * p.k_sb + kvh * p.k_sh;
+  const bf16* __restrict__ Vbh = p.v + b * p.v_sb + kvh * p.v_sh;
+
+  const int q0 = qt * kQTile;
+  const int qrow = q0 + wave * 32 + (lane & 31);
+  const bool row_ok = qrow < p.Nq;
+  const int64_t shift = (int64_t)p.Nk - p.Nq;
+
+  // Q^T fragments: B operand of S^T = K Q^T (k = head dim, n = query).
+  bf16x8 qf[NC];
+  {
+    const int r = row_ok ? qrow : p.Nq - 1;
+    const bf16* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
+  }
+
+  int lo, hi;
+  row_interval(p.mask, b, qrow + shift, p.Nk, lo, hi);
+
+  // Step list.
+  int n_steps = 0, kb_begin = 0, lo_last = 0, hi_first = 0;
+  int bm_row = 0, nf = 0;
+  if constexpr (!BM) {
+    int lo_first, hi_last, t0, t1;
+    const int last_row = min(q0 + kQTile, p.Nq) - 1;
+    row_interval(p.mask, b, q0 + shift, p.Nk, lo_first, hi_first);
+    row_interval(p.mask, b, last_row + shift, p.Nk, t0, t1);
+    lo_last = t0;
+    hi_last = t1;
+    if (hi_last >= lo_first) {
+      kb_begin = (lo_first / kKBlk) * kKBlk;
+      n_steps = (hi_last + 1 - kb_begin + kKBlk - 1) / kKBlk;
+    }
+  } else {
+    const int bb = p.bm_B > 1 ? b : 0, hh = p.bm_H > 1 ? h : 0;
+    bm_row = (bb * p.bm_H + hh) * p.n_qt + qt;
+    nf = p.full_num[bm_row];
+    n_steps = 2 * (nf + p.part_num[bm_row]);
+  }
+  auto step_at = [&](int s) -> Step {
+    Step st;
+    if constexpr (!BM) {
+      st.kb = kb_begin + s * kKBlk;
+      const bool full = st.kb >= lo_last && st.kb + kKBlk - 1 <= hi_first && st.kb + kKBlk <= p.Nk;
+      st.masked = !full;
+      st.use_row_interval = 1;
+    } else {
+      const int t = s >> 1;
+      const int64_t base = (int64_t)bm_row * p.nKt;
+      const int kt = t < nf ? p.full_idx[base + t] : p.part_idx[base + t - nf];
+      st.kb = kt * 128 + (s & 1) * kKBlk;
+      const bool partial = t >= nf;
+      st.use_row_interval = partial;
+      st.masked = partial || st.kb + kKBlk > p.Nk;
+    }
+    return st;
+  };
+
+  TATTN_LDS char* bufK[2] = {smem, smem + 2 * TILE_BYTES};
+  TATTN_LDS char* bufV[2] = {smem + TILE_BYTES, smem + 3 * TILE_BYTES};
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+
+  if (n_steps > 0) {
+    const Step s0 = step_at(0);
+    if (s0.kb >= 0 && s0.kb < p.Nk)
+      issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, s0.kb, p.Nk, bufK[0], bufV[0], wave, lane);
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    wait_vmem();
+    __syncthreads();
+    const Step st = step_at(s);
+    if (s + 1 < n_steps) {
+      const Step sn = step_at(s + 1);
+      if (sn.kb >= 0 && sn.kb < p.Nk)
+        issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, sn.kb, p.Nk, bufK[(s + 1) & 1],
+                            bufV[(s + 1) & 1], wave, lane);
+    }
+    if (st.kb < 0 || st.kb >= p.Nk) continue;  // second half of a ragged last tile
+    const TATTN_LDS char* tK = bufK[s & 1];
+    const TATTN_LDS char* tV = bufV[s & 1];
+
+    // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks) ----
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      sacc[kbk] = f32x16{};
+      const uint32_t row = 32 * kbk + (lane & 31);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 kf = lds_read_b128(tK, tile_off<D>(row, 2 * c + half));
+        sacc[kbk] = mfma32(kf, qf[c], sacc[kbk]);
+      }
+    }
+    // ---- mask (partial steps only) ----
+    if (st.masked) {
+      const int lo_m = st.use_row_interval ? lo : 0;
+      const int hi_m = st.use_row_interval ? hi : p.Nk - 1;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = st.kb + 32 * kbk + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key < lo_m || key > hi_m) sacc[kbk][r] = kNegInf;
+        }
+    }
+    // ---- online softmax ----
+    float mx = sacc[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m_run, mx * p.c2);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
+        l_run += e[i];
+      }
+      pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+    // ---- O^T += V^T P^T ----
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint32_t row0 = 16 * kc + 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t dcol = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+        const uint32_t sub = 8 * (j & 1);
+        const i16x4 v0 = lds_read_tr16(tV, tile_off<D>(row0, dcol >> 3) + sub);
+        const i16x4 v1 = lds_read_tr16(tV, tile_off<D>(row0 + 8, dcol >> 3) + sub);
+        oacc[db] = mfma32(join_tr(v0, v1), pf[kc], oacc[db]);
+      }
+    }
+  }
+
+  // ---- epilogue: O = O_acc / l, LSE = m ln2 + ln l ----
+  const float l_tot = l_run + other_half(l_run);
+  if (row_ok) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* Orow = p.o + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const bf16x2 a = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
+        const bf16x2 c = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        const bf16x4 w = {a[0], a[1], c[0], c[1]};
+        *reinterpret_cast<bf16x4*>(Orow + 32 * db + 8 * r4 + 4 * half) = w;
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] =
+          l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : kNegInf;
+  }
+}
+
+template <int D, bool BM>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_kernel(const FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kKBlk * D * 2];
+  TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
+  int unit = blockIdx.x;
+  if (p.xcd_remap) {
+    // work groups are dealt round-robin to the 8 XCDs: give each XCD a
+    // contiguous range of units (whole heads) so K/V stay in one L2.
+    const int per = gridDim.x >> 3;
+    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  const int slot = unit % p.n_slots;
+  const int bh = unit / p.n_slots;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int kvh = h / p.G;
+  process_tile<D, BM>(p, smem, slot, b, h, kvh);
+  if (p.paired) {
+    const int qt2 = p.n_qt - 1 - slot;
+    if (qt2 != slot) {
+      __syncthreads();
+      process_tile<D, BM>(p, smem, qt2, b, h, kvh);
+    }
+  }
+}
+
+int launch_fwd(const FwdParams& p, int D, bool blockmask, hipStream_t stream) {
+  const long units = (long)p.B * p.Hq * p.n_slots;
+  dim3 grid((unsigned)units), block(kThreads);
+  if (D == 64) {
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, stream, p);
+  } else {
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace tattn

@@ -1,0 +1,63 @@
+// Kernel parameter blocks (passed by value to the kernels), shared by the
+// kernel sources and the host-side C ABI that fills them.
+#pragma once
+
+#include "common.h"
+
+namespace tattn {
+
+// Prefill (dense-mask and BlockMask variants).
+struct FwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn, o_sb, o_sh, o_sn;
+  int B, Hq, Hkv, G, Nq, Nk;
+  float c2;  // scale * log2(e): scores live in base-2 units inside the kernel
+  MaskParams mask;
+  const int32_t* part_num;
+  const int32_t* part_idx;
+  const int32_t* full_num;
+  const int32_t* full_idx;
+  int bm_B, bm_H, nKt;
+  int n_qt;     // query tiles of 128 rows
+  int n_slots;  // work groups per (batch, head)
+  int paired;   // slot i also does tile n_qt-1-i
+  int xcd_remap;
+};
+
+// BlockMask builder.
+struct BmBuildParams {
+  MaskParams mask;
+  const uint8_t* tile_map;
+  int Nq, Nk;
+  int64_t shift;  // Nk - Nq
+  int Bm, Hm, nQt, nKt;
+  int32_t* part_num;
+  int32_t* part_idx;
+  int32_t* full_num;
+  int32_t* full_idx;
+};
+
+// Split-KV paged decode.
+struct DecParams {
+  const bf16* q;
+  int64_t q_sb, q_sh, q_sn;
+  const bf16* kc;
+  const bf16* vc;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* seq_lens;
+  int B, Hq, Hkv, G, Lq, ps, S, chunk;  // chunk: keys per split (multiple of ps)
+  int rows, n_rg;                       // G*Lq query rows per KV head, groups of 64
+  int max_keys;                         // max_pages * page_size
+  int64_t num_pages;                    // pool size (page indices are clamped to it)
+  float c2;
+  MaskParams mask;
+  float* ws_o;
+  float* ws_lse;
+};
+
+}  // namespace tattn
