@@ -1,0 +1,303 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--quick]
+
+Headline: causal prefill B=2 H=16 N=4096 D=64 (bf16 in, fp32 accumulate),
+useful (unmasked) TFLOP/s = 4 * D * (#visible (q, k) pairs) / kernel time, as a
+fraction of the MI355X dense bf16 MFMA peak (2.5 PFLOP/s).  The same run also
+times, each on its own seeded synthetic inputs with inputs resident in HBM:
+
+* decode: split-KV paged decode B=16 Hq=32 Hkv=8, 16 queries over 32768 keys,
+  D=128, 16-token pages (splitkv + combine), KV-read GB/s = B*Hkv*Nk*D*2 bytes
+  * 2 (K and V) / time, as a fraction of the 8 TB/s HBM peak;
+* the other prefill workloads (window+document and block-diffusion at
+  B=1 H=32 N=8192 D=128, block-sparse GQA at N=32768), in TFLOP/s.
+
+Each kernel is timed with HIP events recorded on the stream it is launched on
+(torch's current stream, which the binding passes to the library); K timed
+launches after W warm-up launches, bracketed by synchronisation.  The CPU
+baseline is the fp64 oracle timed on this host's cores over a bounded sample
+of the headline workload.  One JSON line is printed on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_launches(fn, steps, warmup):
+    """Average per-launch kernel time (ms) from HIP events on the current stream,
+    and the wall time of the whole timed region (ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    outer0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return sum(per) / len(per), min(per), outer0.elapsed_time(outer1)
+
+
+def causal_pairs(N):
+    return N * (N + 1) // 2
+
+
+def visible_pairs_dense(lo, hi):
+    import numpy as np
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def bench_prefill_causal(T, W, steps, warmup):
+    import torch
+    wl = W.causal_b2h16n4096d64()
+    q, k, v = (wl.tensors[x].cuda() for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 16, 4096, dtype=torch.float32, device="cuda")
+    mask = T.Mask(causal=True)
+    desc = mask.desc()
+    fn = lambda: T.attn_fwd(q, k, v, o, lse, wl.scale, desc)
+    avg, best, wall = time_launches(fn, steps, warmup)
+    flops = 4.0 * 64 * 2 * 16 * causal_pairs(4096)
+    return wl, dict(avg_ms=avg, min_ms=best, wall_ms=wall, flops=flops)
+
+
+def bench_prefill_others(T, W, steps, warmup):
+    import numpy as np
+    import torch
+    out = []
+    # window + document and block-diffusion, B=1 H=32 N=8192 D=128
+    for name in ("window_doc_b1h32n8192d128", "blockdiff_b1h32n8192d128"):
+        wl = W.FULL_SIZE[name]()
+        q, k, v = (wl.tensors[x].cuda() for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(1, 32, 8192, dtype=torch.float32, device="cuda")
+        N = 8192
+        p = np.arange(N)
+        if name.startswith("window"):
+            lens = wl.mask["doc_lengths"][0]
+            starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            off = torch.tensor(starts, dtype=torch.int32, device="cuda")[None]
+            mask = T.Mask(window=(512, 512), doc_offsets=off)
+            d = np.searchsorted(starts, p, side="right") - 1
+            lo = np.maximum(p - 512, starts[d])
+            hi = np.minimum(p + 512, starts[d + 1] - 1)
+        else:
+            mask = T.Mask(block_size=16)
+            lo = np.zeros(N, dtype=np.int64)
+            hi = np.minimum((p // 16 + 1) * 16 - 1, N - 1)
+        desc = mask.desc()
+        fn = lambda: T.attn_fwd(q, k, v, o, lse, wl.scale, desc)
+        avg, best, wall = time_launches(fn, steps, warmup)
+        flops = 4.0 * 128 * 32 * visible_pairs_dense(lo, hi)
+        out.append(dict(workload=name, avg_ms=avg, min_ms=best, tflops=flops / avg / 1e9,
+                        frac=flops / avg / 1e9 / PEAK_BF16_TFLOPS))
+        del q, k, v, o, lse
+    # block-sparse GQA, N=32768
+    wl = W.blockmask_gqa_b1h32kv8n32768d128()
+    q, k, v = (wl.tensors[x].cuda() for x in ("q", "k", "v"))
+    N = 32768
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 32, N, dtype=torch.float32, device="cuda")
+    tm = wl.mask["tile_map"]
+    bm = T.BlockMask(1, 1, N, N)
+    tmg = tm[None, None].contiguous().cuda()
+    build = lambda: T.attn_build_blockmask(bm, 1, N, N, tile_map=tmg)
+    b_avg, _, _ = time_launches(build, steps, warmup)
+    desc = T.Mask(causal=True).desc()
+    fn = lambda: T.attn_fwd_blockmask(q, k, v, o, bm, lse, wl.scale, desc)
+    avg, best, wall = time_launches(fn, steps, warmup)
+    n_full = int((tm == W.TILE_FULL).sum())
+    n_diag = int((tm == W.TILE_PARTIAL).sum())
+    pairs = n_full * 128 * 128 + n_diag * (128 * 129 // 2)
+    flops = 4.0 * 128 * 32 * pairs
+    out.append(dict(workload=wl.name, avg_ms=avg, min_ms=best, tflops=flops / avg / 1e9,
+                    frac=flops / avg / 1e9 / PEAK_BF16_TFLOPS, blockmask_build_ms=b_avg))
+    return out
+
+
+def bench_decode(T, W, steps, warmup):
+    import torch
+    wl = W.decode_b16h32kv8q16k32768d128()
+    t = wl.tensors
+    B, Hq, Hkv, Lq, Nk, D = 16, 32, 8, 16, 32768, 128
+    q = t["q"].cuda()
+    kp, vp = t["k_pool"].cuda(), t["v_pool"].cuda()
+    bt, sl = t["block_table"].cuda(), t["seq_lens"].cuda()
+    del wl, t
+    S = T.attn_decode_num_splits(B, Hkv, 2048)
+    ws_o = torch.empty(B, Hq, Lq, S, D, dtype=torch.float32, device="cuda")
+    ws_l = torch.empty(B, Hq, Lq, S, dtype=torch.float32, device="cuda")
+    o = torch.empty(B, Hq, Lq, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    def split():
+        T.attn_decode_splitkv(q, kp, vp, bt, sl, 2048, S, ws_o, ws_l, scale)
+
+    def comb():
+        T.attn_decode_combine(ws_o, ws_l, o, lse)
+
+    def both():
+        split()
+        comb()
+    s_avg, s_min, _ = time_launches(split, steps, warmup)
+    c_avg, _, _ = time_launches(comb, steps, warmup)
+    avg, best, wall = time_launches(both, steps, warmup)
+    kv_bytes = float(B * Hkv * Nk * D * 2 * 2)
+    return dict(avg_ms=avg, min_ms=best, wall_ms=wall, splitkv_ms=s_avg, combine_ms=c_avg,
+                splits=S, kv_bytes=kv_bytes)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle on this host, on a bounded sample of the headline workload:
+    whole (batch, head) slices of causal B=2 H=16 N=4096 D=64, in order, until the
+    time budget is spent.  Useful FLOP as for the GPU."""
+    import numpy as np
+    import oracle
+    from oracle import masks as M
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    wl = W.causal_b2h16n4096d64()
+    q = wl.tensors["q"].double().numpy()
+    k = wl.tensors["k"].double().numpy()
+    v = wl.tensors["v"].double().numpy()
+    mod = M.causal(4096, 4096)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(2):
+        for h in range(16):
+            for r0 in range(0, 4096, 512):
+                rows = np.arange(r0, r0 + 512)
+                oracle.attention_rows(q, k, v, wl.scale, mod, b, h, rows)
+            flops += 4.0 * 64 * causal_pairs(4096)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{heads} of 32 (batch, head) slices of causal_b2h16n4096d64, fp64 NumPy, "
+                       f"{dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="headline prefill only")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="profiling helper: run one kernel family only (copy = a plain "
+                         "device-to-device copy of 1 GiB, for calibrating HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tiled_attention_attn_amd as T
+    import workloads as W
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({props.gcnArchName}), {props.multi_processor_count} CUs")
+    if args.only == "copy":
+        n = 1 << 29  # 1 GiB of bf16 read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        avg, _, _ = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+        log(f"copy 1 GiB: {avg*1e3:.1f} us, {2 * n * 2 / avg / 1e6:.0f} GB/s (read + write)")
+        return
+    if args.only == "decode":
+        dec = bench_decode(T, W, args.steps, args.warmup)
+        log(f"decode: {dec['avg_ms']*1e3:.1f} us (splitkv {dec['splitkv_ms']*1e3:.1f} + combine "
+            f"{dec['combine_ms']*1e3:.1f}), {dec['kv_bytes'] / dec['avg_ms'] / 1e6:.0f} GB/s")
+        return
+
+    wl, pf = bench_prefill_causal(T, W, args.steps, args.warmup)
+    tflops = pf["flops"] / pf["avg_ms"] / 1e9
+    log(f"prefill causal_b2h16n4096d64: {pf['avg_ms']*1e3:.1f} us/launch, {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": "attention TFLOP/s (unmasked) & % bf16 MFMA peak; decode KV GB/s & % HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["wall_ms"] / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal_b2h16n4096d64", "B": 2, "H": 16, "N": 4096, "D": 64,
+                   "mask": "causal", "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_kernel<64,false>",
+                     "kernel_us": round(pf["avg_ms"] * 1e3, 2)},
+    }
+    if args.only == "prefill":
+        return
+    if not args.quick:
+        dec = bench_decode(T, W, args.steps, args.warmup)
+        gbs = dec["kv_bytes"] / dec["avg_ms"] / 1e6
+        log(f"decode: {dec['avg_ms']*1e3:.1f} us (splitkv {dec['splitkv_ms']*1e3:.1f} + combine "
+            f"{dec['combine_ms']*1e3:.1f}), {gbs:.0f} GB/s, S={dec['splits']}")
+        s_gbs = dec["kv_bytes"] / dec["splitkv_ms"] / 1e6
+        result["decode"] = {
+            "workload": "decode_b16h32kv8q16k32768d128", "value": round(gbs, 1), "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "us_per_step": round(dec["avg_ms"] * 1e3, 2),
+            "splitkv_us": round(dec["splitkv_ms"] * 1e3, 2),
+            "combine_us": round(dec["combine_ms"] * 1e3, 2), "num_splits": dec["splits"],
+            "roofline": {"bound": "hbm", "achieved": round(s_gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(s_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "decode_kernel<128>"},
+        }
+        others = bench_prefill_others(T, W, args.steps, args.warmup)
+        for o in others:
+            log(f"prefill {o['workload']}: {o['avg_ms']*1e3:.1f} us, {o['tflops']:.1f} TFLOP/s")
+        result["prefill_other"] = [{k: (round(v, 4) if isinstance(v, float) else v)
+                                    for k, v in o.items()} for o in others]
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline()
+        log(f"cpu oracle: {cb['value']:.4f} TFLOP/s on {cb['cores']} threads ({cb['sample']})")
+        cb["value"] = round(cb["value"], 6)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -184,8 +184,9 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3],
  *   seq_lens    device int32 [B]: key count of each sequence, the Lq new
  *               tokens included (0 <= seq_lens[b] <= max_pages * page_size)
  *   max_pages   pages of the block table a sequence may use (<= bt_stride)
- *   num_splits  S >= 1.  Split s covers keys [s*C, min((s+1)*C, seq_len))
- *               with C = page_size * ceil(max_pages / S).
+ *   num_splits  S >= 1 with ceil(max_pages / S) <= 2048 (a split's block-
+ *               table entries are staged on chip).  Split s covers keys
+ *               [s*C, min((s+1)*C, seq_len)) with C = page_size * ceil(max_pages / S).
  *   mask        NULL = causal; else CAUSAL / WINDOW / BLOCK_CAUSAL flags
  *               (DOCUMENT is rejected).  Query t of sequence b sits at
  *               position seq_lens[b] - Lq + t.

@@ -212,12 +212,15 @@ size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits) {
 int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
   if (B <= 0 || Hkv <= 0 || max_pages <= 0) return 1;
   if (num_cus <= 0) num_cus = 256;
-  // Two resident work groups per compute unit; round the work-group count up
-  // to a whole number of waves of the machine.
+  // One resident work group per compute unit (the decode kernel's LDS ring
+  // fills most of a CU's LDS): enough splits for every CU, no more splits
+  // than pages, and at most 2048 pages per split.
   const long units = (long)B * Hkv;
-  const long target = 2L * num_cus;
+  const long target = num_cus;
   long s = (target + units - 1) / units;
   if (s < 1) s = 1;
+  const long min_s = (max_pages + 2047) / 2048;
+  if (s < min_s) s = min_s;
   if (s > max_pages) s = max_pages;
   return (int)s;
 }
@@ -243,6 +246,8 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
     return ATTN_ERR_ALIGN;
   if ((st = check_scale(scale))) return st;
   if (num_splits < 1 || num_splits > 65536) return ATTN_ERR_WORKSPACE;
+  // A split's block-table entries are staged in LDS: at most 2048 pages each.
+  if ((max_pages + num_splits - 1) / num_splits > 2048) return ATTN_ERR_WORKSPACE;
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;

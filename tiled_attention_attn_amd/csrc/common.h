@@ -59,12 +59,54 @@ __device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
 }
 
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's
-// 16 bytes land at lds_wave_base + 16 * l.  lds_wave_base must be uniform.
-__device__ __forceinline__ void dma16(const void* gsrc, TATTN_LDS void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+// 16 bytes land at LDS address lds_wave_base + 16 * l; lds_wave_base must be
+// wave-uniform.  Issued from inline assembly on purpose: the compiler then
+// does not track these copies, so it adds no blanket vmcnt(0) wait in front
+// of LDS reads it cannot prove disjoint (it does so for ds_read_b64_tr_b16),
+// which would serialise the pipeline.  Completion is ordered explicitly by
+// the callers: wait_vmem_le<N>() in each wave, then lds_barrier().  The
+// instruction writes no VGPR, reads its address registers at issue, and the
+// memory clobber keeps the compiler from moving other memory accesses across.
+// The compiler writes M0 (the LDS address) right before the block; GFX9-family
+// hardware needs one wait state between an SALU write of M0 and an LDS-DMA
+// instruction that reads it (the compiler's hazard recognizer cannot see into
+// the block), hence the s_nop.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "{m0}"(lds_wave_base)
+               : "memory");
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }  // vmcnt(0)
+// 32-bit LDS address of an LDS pointer.
+__device__ __forceinline__ uint32_t lds_addr(const TATTN_LDS void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+__device__ __forceinline__ void wait_vmem() {  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x3f70);
+  asm volatile("" ::: "memory");
+}
+
+// Work-group barrier for LDS hand-off only.  __syncthreads() adds a
+// work-group release fence, which waits for every outstanding vector-memory
+// operation (vmcnt(0)) -- including the asynchronous LDS copies of later
+// pipeline stages.  Here each wave waits for its own copies explicitly
+// (wait_vmem_le), finishes its LDS reads (lgkmcnt(0)) and then meets the
+// others; the memory clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this
+// wave are outstanding (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 
 // ---- cross-lane ----------------------------------------------------------------
 // Value of the lane 32 positions away (lanes l and l^32 exchange).

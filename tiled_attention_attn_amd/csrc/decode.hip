@@ -24,6 +24,8 @@ namespace tattn {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecKBlk = 64;
+constexpr int kDecStages = 4;           // LDS pipeline depth (64-key stages)
+constexpr int kDecMaxSplitPages = 2048;  // block-table entries of one split, kept in LDS
 
 template <int D> struct DSwz;
 template <> struct DSwz<64> {
@@ -40,7 +42,7 @@ __device__ __forceinline__ uint32_t dtile_off(uint32_t row, uint32_t chunk) {
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
 template <int D>
-__global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kDecThreads)
 decode_kernel(const DecParams p) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per key row
   constexpr int INSTS = kDecKBlk * CPR / 64;       // wave instructions per tile
@@ -48,10 +50,14 @@ decode_kernel(const DecParams p) {
   constexpr int TILE_BYTES = kDecKBlk * D * 2;
   constexpr int NC = D / 32;   // d-chunks of the QK MFMA (K = 32)
   constexpr int NDB = D / 16;  // d-blocks of the PV MFMA (M = 16)
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE_BYTES];
+  constexpr int NST = kDecStages;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * TILE_BYTES];
+  __shared__ int s_pages[kDecMaxSplitPages];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
-  TATTN_LDS char* bufK[2] = {smem, smem + 2 * TILE_BYTES};
-  TATTN_LDS char* bufV[2] = {smem + TILE_BYTES, smem + 3 * TILE_BYTES};
+  auto bufK = [&](int st) -> TATTN_LDS char* { return smem + (st % NST) * 2 * TILE_BYTES; };
+  auto bufV = [&](int st) -> TATTN_LDS char* {
+    return smem + (st % NST) * 2 * TILE_BYTES + TILE_BYTES;
+  };
 
   const int s = blockIdx.x % p.S, rg = blockIdx.x / p.S;
   const int kvh = blockIdx.y, b = blockIdx.z;
@@ -78,18 +84,18 @@ decode_kernel(const DecParams p) {
 
   // Keys any row of this group can see: rows differ only in t, and the
   // interval ends never decrease with t, so t = 0 and t = Lq-1 bound them.
-  int klo = k_end, khi = k_begin - 1;
+  // A split that starts at or past the end of the sequence has no steps.
+  int n_steps = 0, kb0 = k_begin;
   if (seq_len > 0 && k_end > k_begin) {
     int a0, a1, c0, c1;
     row_interval(p.mask, b, (int64_t)seq_len - p.Lq, seq_len, a0, a1);
     row_interval(p.mask, b, (int64_t)seq_len - 1, seq_len, c0, c1);
-    klo = max(a0, k_begin);
-    khi = min(c1, k_end - 1);
-  }
-  int n_steps = 0, kb0 = k_begin;
-  if (khi >= klo) {
-    kb0 = k_begin + ((klo - k_begin) / kDecKBlk) * kDecKBlk;
-    n_steps = (khi + 1 - kb0 + kDecKBlk - 1) / kDecKBlk;
+    const int klo = max(a0, k_begin);  // >= k_begin
+    const int khi = min(c1, k_end - 1);
+    if (khi >= klo) {
+      kb0 = k_begin + ((klo - k_begin) / kDecKBlk) * kDecKBlk;
+      n_steps = (khi + 1 - kb0 + kDecKBlk - 1) / kDecKBlk;
+    }
   }
   // Rows of this wave that are unmasked on a whole step: bounds over the wave.
   int wlo = row_ok ? lo : -0x3fffffff, whi = row_ok ? hi : 0x3fffffff;
@@ -105,21 +111,20 @@ decode_kernel(const DecParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 32 * c);
   }
-
+  // The split's block-table entries go to LDS once, so the pipelined loop
+  // below issues no vector-memory loads other than the K/V copies.
   const int32_t* bt_row = p.bt + b * p.bt_stride;
+  const int page0 = k_begin / p.ps;
+  const int n_split_pages = k_end > k_begin ? (k_end - 1) / p.ps - page0 + 1 : 0;
+  for (int i = tid; i < n_split_pages; i += kDecThreads) {
+    const int page = bt_row[page0 + i];
+    s_pages[i] = page < 0 ? 0 : (page >= p.num_pages ? (int)p.num_pages - 1 : page);
+  }
+  wait_vmem();  // Q fragments and page entries
+  __syncthreads();
+
   const int64_t row_stride = (int64_t)p.Hkv * D;  // elements between slots of a page
-  // Pages of the key rows this lane copies in a step.
-  int pg[PER_WAVE];
-  auto load_pages = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      int key = kb + ((wave * PER_WAVE + i) * 64 + lane) / CPR;
-      key = key < seq_len ? key : seq_len - 1;
-      const int page = bt_row[key / p.ps];
-      pg[i] = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
-    }
-  };
-  auto issue = [&](int kb, int buf) {
+  auto issue = [&](int kb, int st) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int inst = wave * PER_WAVE + i;
@@ -127,34 +132,37 @@ decode_kernel(const DecParams p) {
       const uint32_t row = slot / CPR;
       const uint32_t chunk = (slot % CPR) ^ DSwz<D>::f(row);
       int key = kb + (int)row;
-      key = key < seq_len ? key : seq_len - 1;
-      const int64_t off = ((int64_t)pg[i] * p.ps + key % p.ps) * row_stride + kvh * D + chunk * 8;
-      dma16(p.kc + off, bufK[buf] + inst * 1024);
-      dma16(p.vc + off, bufV[buf] + inst * 1024);
+      key = key < k_end ? key : k_end - 1;
+      int pidx = key / p.ps - page0;  // in [0, n_split_pages) for every issued step
+      pidx = pidx < 0 ? 0 : (pidx >= n_split_pages ? n_split_pages - 1 : pidx);
+      const int page = s_pages[pidx];
+      const int64_t off = ((int64_t)page * p.ps + key % p.ps) * row_stride + kvh * D + chunk * 8;
+      const uint32_t loff = __builtin_amdgcn_readfirstlane(inst * 1024);
+      dma16(p.kc + off, lds_addr(bufK(st)) + loff);
+      dma16(p.vc + off, lds_addr(bufV(st)) + loff);
     }
   };
+  constexpr int LOADS = 2 * PER_WAVE;  // copies per wave per step
 
   float m_run = kNegInf, l_run = 0.f;
   f32x4 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x4{};
 
-  if (n_steps > 0) {
-    load_pages(kb0);
-    wait_vmem();
-    issue(kb0, 0);
-    if (n_steps > 1) load_pages(kb0 + kDecKBlk);
-  }
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < n_steps) issue(kb0 + st * kDecKBlk, st);
   for (int st = 0; st < n_steps; ++st) {
     const int kb = kb0 + st * kDecKBlk;
-    wait_vmem();
-    __syncthreads();
-    if (st + 1 < n_steps) {
-      issue(kb + kDecKBlk, (st + 1) & 1);
-      if (st + 2 < n_steps) load_pages(kb + 2 * kDecKBlk);
-    }
-    const TATTN_LDS char* tK = bufK[st & 1];
-    const TATTN_LDS char* tV = bufV[st & 1];
+    // Copies issued after step st's: those of steps st+1 .. min(st+NST-2, n-1).
+    const int later = min(NST - 2, n_steps - 1 - st);
+    if (later >= 2) wait_vmem_le<2 * LOADS>();
+    else if (later == 1) wait_vmem_le<LOADS>();
+    else wait_vmem();
+    lds_barrier();
+    if (st + NST - 1 < n_steps) issue(kb + (NST - 1) * kDecKBlk, st + NST - 1);
+    const TATTN_LDS char* tK = bufK(st);
+    const TATTN_LDS char* tV = bufV(st);
 
     f32x4 sacc[4];
 #pragma unroll

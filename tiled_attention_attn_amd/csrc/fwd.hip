@@ -34,6 +34,11 @@ namespace tattn {
 constexpr int kQTile = 128;
 constexpr int kKBlk = 64;
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;  // log2 headroom before the reference max moves
+
+// Pipeline depth (LDS stages) per head dim: 3 x 16 KB at D=64, 2 x 32 KB at
+// D=128, so two work groups fit in one CU's LDS.
+template <int D> struct Stages { static constexpr int value = D == 64 ? 3 : 2; };
 
 // XOR swizzle of the 16-byte chunks of tile row r (see the header comment).
 template <int D> struct Swz;
@@ -72,12 +77,13 @@ __device__ __forceinline__ void issue_tile_loads(const bf16* __restrict__ Kbh,
     const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
     int key = kb + (int)row;
     key = key < Nk ? key : Nk - 1;
-    dma16(Kbh + (int64_t)key * k_sn + chunk * 8, ldsK + inst * 1024);
-    dma16(Vbh + (int64_t)key * v_sn + chunk * 8, ldsV + inst * 1024);
+    const uint32_t off = __builtin_amdgcn_readfirstlane(inst * 1024);
+    dma16(Kbh + (int64_t)key * k_sn + chunk * 8, lds_addr(ldsK) + off);
+    dma16(Vbh + (int64_t)key * v_sn + chunk * 8, lds_addr(ldsV) + off);
   }
 }
 
-template <int D, bool BM>
+template <int D, bool BM, int NST>
 __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
                                              int b, int h, int kvh) {
   constexpr int TILE_BYTES = kKBlk * D * 2;
@@ -102,6 +108,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     const bf16* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
+    // Complete these loads here, so the waits inside the step loop only ever
+    // concern the asynchronous K/V copies.
+    wait_vmem();
   }
 
   int lo, hi;
@@ -146,32 +155,46 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     return st;
   };
 
-  TATTN_LDS char* bufK[2] = {smem, smem + 2 * TILE_BYTES};
-  TATTN_LDS char* bufV[2] = {smem + TILE_BYTES, smem + 3 * TILE_BYTES};
+  // Ring of NST stages, each one K tile and one V tile; the loads of step
+  // s + NST - 1 are in flight while step s computes.
+  auto bufK = [&](int s) -> TATTN_LDS char* { return smem + (s % NST) * 2 * TILE_BYTES; };
+  auto bufV = [&](int s) -> TATTN_LDS char* { return smem + (s % NST) * 2 * TILE_BYTES + TILE_BYTES; };
+  // Every step issues the same number of copies (ragged tails clamp their
+  // rows), so the vmcnt bookkeeping below is exact.
+  auto load_step = [&](int s) {
+    int kb = step_at(s).kb;
+    kb = kb < 0 ? 0 : kb;
+    issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, kb, p.Nk, bufK(s), bufV(s), wave, lane);
+  };
+  constexpr int LOADS = 2 * (kKBlk * D / 8 / 64) / (kThreads / 64);  // copies per wave per step
 
   float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
 
-  if (n_steps > 0) {
-    const Step s0 = step_at(0);
-    if (s0.kb >= 0 && s0.kb < p.Nk)
-      issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, s0.kb, p.Nk, bufK[0], bufV[0], wave, lane);
+  if (p.Nk > 0) {
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < n_steps) load_step(s);
   }
   for (int s = 0; s < n_steps; ++s) {
-    wait_vmem();
-    __syncthreads();
-    const Step st = step_at(s);
-    if (s + 1 < n_steps) {
-      const Step sn = step_at(s + 1);
-      if (sn.kb >= 0 && sn.kb < p.Nk)
-        issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, sn.kb, p.Nk, bufK[(s + 1) & 1],
-                            bufV[(s + 1) & 1], wave, lane);
+    // Loads issued after step s's: those of steps s+1 .. min(s+NST-2, n-1).
+    if constexpr (NST == 3) {
+      if (s + 1 < n_steps) wait_vmem_le<LOADS>(); else wait_vmem();
+    } else if constexpr (NST == 4) {
+      if (s + 2 < n_steps) wait_vmem_le<2 * LOADS>();
+      else if (s + 1 < n_steps) wait_vmem_le<LOADS>();
+      else wait_vmem();
+    } else {
+      wait_vmem();
     }
+    lds_barrier();
+    if (s + NST - 1 < n_steps) load_step(s + NST - 1);
+    const Step st = step_at(s);
     if (st.kb < 0 || st.kb >= p.Nk) continue;  // second half of a ragged last tile
-    const TATTN_LDS char* tK = bufK[s & 1];
-    const TATTN_LDS char* tV = bufV[s & 1];
+    const TATTN_LDS char* tK = bufK(s);
+    const TATTN_LDS char* tV = bufV(s);
 
     // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks) ----
     f32x16 sacc[2];
@@ -197,20 +220,25 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
           if (key < lo_m || key > hi_m) sacc[kbk][r] = kNegInf;
         }
     }
-    // ---- online softmax ----
+    // ---- online softmax with a lazily moved reference max ----
+    // Probabilities are taken against m_run; m_run (and O, l) are only
+    // rescaled when some row's max exceeds it by more than 2^kLazy, so
+    // exp2(s - m_run) <= 2^kLazy stays well inside fp32 / bf16 range.
     float mx = sacc[0][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx * p.c2);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    mx = fmaxf(mx, other_half(mx)) * p.c2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
 
     bf16x8 pf[4];
 #pragma unroll
@@ -262,7 +290,8 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
 template <int D, bool BM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * kKBlk * D * 2];
+  constexpr int NST = Stages<D>::value;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * kKBlk * D * 2];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.xcd_remap) {
@@ -275,12 +304,12 @@ fwd_kernel(const FwdParams p) {
   const int bh = unit / p.n_slots;
   const int h = bh % p.Hq, b = bh / p.Hq;
   const int kvh = h / p.G;
-  process_tile<D, BM>(p, smem, slot, b, h, kvh);
+  process_tile<D, BM, NST>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      process_tile<D, BM>(p, smem, qt2, b, h, kvh);
+      process_tile<D, BM, NST>(p, smem, qt2, b, h, kvh);
     }
   }
 }
