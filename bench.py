@@ -269,9 +269,7 @@ def main():
                      "traffic": None, "kernel": "fwd_kernel<64,false>",
                      "kernel_us": round(pf["avg_ms"] * 1e3, 2)},
     }
-    if args.only == "prefill":
-        return
-    if not args.quick:
+    if not args.quick and args.only == "all":
         dec = bench_decode(T, W, args.steps, args.warmup)
         gbs = dec["kv_bytes"] / dec["avg_ms"] / 1e6
         log(f"decode: {dec['avg_ms']*1e3:.1f} us (splitkv {dec['splitkv_ms']*1e3:.1f} + combine "
@@ -286,6 +284,7 @@ def main():
                          "unit": "GB/s", "frac": round(s_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                          "kernel": "decode_kernel<128>"},
         }
+    if not args.quick:
         others = bench_prefill_others(T, W, args.steps, args.warmup)
         for o in others:
             log(f"prefill {o['workload']}: {o['avg_ms']*1e3:.1f} us, {o['tflops']:.1f} TFLOP/s")

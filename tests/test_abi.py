@@ -117,7 +117,7 @@ def test_blockmask_and_decode_argument_errors(T):
     assert dec(B=0) == 0
     assert lib.attn_decode_combine(None, 16, 1, 1, 1, 1, 64, 32, qs, None, None) == -1
     assert lib.attn_decode_combine(16, 16, 1, 1, 1, 0, 64, 32, qs, None, None) == -8
-    assert lib.attn_decode_num_splits(16, 8, 2048, 256) == 2   # one work group per CU
+    assert lib.attn_decode_num_splits(16, 8, 2048, 256) == 4   # two work groups per CU
     assert lib.attn_decode_num_splits(1, 1, 3, 256) == 3        # never more splits than pages
     assert lib.attn_decode_num_splits(1, 300, 10000, 256) == 5  # at most 2048 pages per split
     assert dec(S=1, maxp=4097, bts=4097) == -8                  # 4097 pages in one split

@@ -212,11 +212,11 @@ size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits) {
 int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
   if (B <= 0 || Hkv <= 0 || max_pages <= 0) return 1;
   if (num_cus <= 0) num_cus = 256;
-  // One resident work group per compute unit (the decode kernel's LDS ring
-  // fills most of a CU's LDS): enough splits for every CU, no more splits
-  // than pages, and at most 2048 pages per split.
+  // Two resident work groups per compute unit (72 KB of LDS each): enough
+  // splits for two per CU, no more splits than pages, and at most 2048 pages
+  // per split.
   const long units = (long)B * Hkv;
-  const long target = num_cus;
+  const long target = 2L * num_cus;
   long s = (target + units - 1) / units;
   if (s < 1) s = 1;
   const long min_s = (max_pages + 2047) / 2048;

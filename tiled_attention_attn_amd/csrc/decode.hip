@@ -23,9 +23,13 @@
 namespace tattn {
 
 constexpr int kDecThreads = 256;
-constexpr int kDecKBlk = 64;
-constexpr int kDecStages = 4;           // LDS pipeline depth (64-key stages)
+constexpr int kDecStages = 4;            // LDS pipeline depth
 constexpr int kDecMaxSplitPages = 2048;  // block-table entries of one split, kept in LDS
+// Keys per step: the K + V ring (kDecStages stages) is 64 KB at both head
+// dims.  Asynchronous LDS copies only ever target the first 64 KB of a work
+// group's LDS (no copy into LDS at 64 KB or above is relied on), and 64 KB of
+// ring plus the 8 KB page table lets two work groups share a CU.
+template <int D> struct DecKBlk { static constexpr int value = D == 64 ? 64 : 32; };
 
 template <int D> struct DSwz;
 template <> struct DSwz<64> {
@@ -44,6 +48,9 @@ __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x,
 template <int D>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(const DecParams p) {
+  constexpr int kDecKBlk = DecKBlk<D>::value;
+  constexpr int NKB = kDecKBlk / 16;               // 16-key blocks per step
+  constexpr int NKC = kDecKBlk / 32;               // 32-key PV chunks per step
   constexpr int CPR = D / 8;                       // 16-byte chunks per key row
   constexpr int INSTS = kDecKBlk * CPR / 64;       // wave instructions per tile
   constexpr int PER_WAVE = INSTS / (kDecThreads / 64);
@@ -164,9 +171,9 @@ decode_kernel(const DecParams p) {
     const TATTN_LDS char* tK = bufK(st);
     const TATTN_LDS char* tV = bufV(st);
 
-    f32x4 sacc[4];
+    f32x4 sacc[NKB];
 #pragma unroll
-    for (int kb16 = 0; kb16 < 4; ++kb16) {
+    for (int kb16 = 0; kb16 < NKB; ++kb16) {
       sacc[kb16] = f32x4{};
       const uint32_t row = 16 * kb16 + col;
 #pragma unroll
@@ -176,7 +183,7 @@ decode_kernel(const DecParams p) {
     const bool full = kb >= wlo && kb + kDecKBlk - 1 <= whi;
     if (!full) {
 #pragma unroll
-      for (int kb16 = 0; kb16 < 4; ++kb16)
+      for (int kb16 = 0; kb16 < NKB; ++kb16)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kb + 16 * kb16 + 4 * grp + r;
@@ -185,7 +192,7 @@ decode_kernel(const DecParams p) {
     }
     float mx = sacc[0][0];
 #pragma unroll
-    for (int kb16 = 0; kb16 < 4; ++kb16)
+    for (int kb16 = 0; kb16 < NKB; ++kb16)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb16][r]);
     mx = fmaxf(mx, xor_lane(mx, 16));
@@ -197,9 +204,9 @@ decode_kernel(const DecParams p) {
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
-    bf16x8 pf[2];
+    bf16x8 pf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -209,7 +216,7 @@ decode_kernel(const DecParams p) {
       pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       const uint32_t r1 = 32 * kc + 4 * grp + (col >> 2);
       const uint32_t r2 = r1 + 16;
 #pragma unroll

@@ -232,7 +232,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     mx = fmaxf(mx, other_half(mx)) * p.c2;
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+      // A row that has seen no key yet has O = 0 and l = 0: alpha must be 0
+      // there, also when its m_new is still -inf (exp2(-inf - -inf) is NaN).
+      const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
