@@ -25,7 +25,7 @@
  *   B/H/N dimensions in memory is accepted, so both [B, H, N, D] and
  *   [B, N, H, D] layouts pass without a copy (FlashAttention 2 article,
  *   section 2).  Strides must be multiples of 8 elements and base pointers
- *   16-byte aligned.
+ *   16-byte aligned; the sequence (n) strides of K and V stay below 2^25.
  * - LSE is fp32 [B, Hq, Nq], contiguous, natural log, scale included.  A row
  *   that sees no key gets O = 0 and LSE = -inf.  LSE pointers may be NULL
  *   where noted (then it is not written).

@@ -74,6 +74,8 @@ int check_common(const void* q, const int64_t* qs, const void* k, const int64_t*
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
     return ATTN_ERR_ALIGN;
+  // The prefill kernel addresses a 64-row K/V tile with 32-bit byte offsets.
+  if (ks[2] >= (int64_t)1 << 25 || vs[2] >= (int64_t)1 << 25) return ATTN_ERR_STRIDE;
   return check_scale(scale);
 }
 

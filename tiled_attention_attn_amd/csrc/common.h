@@ -78,6 +78,16 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) 
                : "memory");
 }
 
+// The same copy addressed as a uniform 64-bit base (SGPR pair) plus a 32-bit
+// per-lane byte offset: no per-lane 64-bit address arithmetic is needed.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff_bytes,
+                                         uint32_t lds_wave_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff_bytes), "s"(sbase), "{m0}"(lds_wave_base)
+               : "memory");
+}
+
 // 32-bit LDS address of an LDS pointer.
 __device__ __forceinline__ uint32_t lds_addr(const TATTN_LDS void* p) {
   return (uint32_t)(uintptr_t)p;

@@ -27,6 +27,8 @@
 //    every group does the same amount of work; the group -> (batch, head)
 //    mapping keeps all tiles of a head (and of a GQA group) on one XCD so its
 //    K/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "params.h"
 
 namespace tattn {
@@ -60,35 +62,19 @@ struct Step {
   int use_row_interval;  // 1: the row's own mask interval; 0: only k < Nk
 };
 
-template <int D>
-__device__ __forceinline__ void issue_tile_loads(const bf16* __restrict__ Kbh,
-                                                 const bf16* __restrict__ Vbh, int64_t k_sn,
-                                                 int64_t v_sn, int kb, int Nk,
-                                                 TATTN_LDS char* ldsK, TATTN_LDS char* ldsV,
-                                                 int wave, int lane) {
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int INSTS = kKBlk * CPR / 64;         // wave instructions per tile
-  constexpr int PER_WAVE = INSTS / (kThreads / 64);
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = wave * PER_WAVE + i;
-    const int slot = inst * 64 + lane;
-    const uint32_t row = slot / CPR;
-    const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
-    int key = kb + (int)row;
-    key = key < Nk ? key : Nk - 1;
-    const uint32_t off = __builtin_amdgcn_readfirstlane(inst * 1024);
-    dma16(Kbh + (int64_t)key * k_sn + chunk * 8, lds_addr(ldsK) + off);
-    dma16(Vbh + (int64_t)key * v_sn + chunk * 8, lds_addr(ldsV) + off);
-  }
-}
-
 template <int D, bool BM, int NST>
 __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
                                              int b, int h, int kvh) {
   constexpr int TILE_BYTES = kKBlk * D * 2;
-  constexpr int NC = D / 16;   // d-chunks of the QK MFMA
-  constexpr int NDB = D / 32;  // d-blocks of the PV MFMA
+  constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
+  constexpr int NC = D / 16;                   // d-chunks of the QK MFMA
+  constexpr int NDB = D / 32;                  // d-blocks of the PV MFMA
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  constexpr int PER_WAVE = kKBlk * CPR / 64 / (kThreads / 64);  // copies per wave per tile
+  constexpr int LOADS = 2 * PER_WAVE;          // K + V copies per wave per step
+  // The swizzle repeats every KC_PERIOD 16-row key chunks: 32 rows at D=64,
+  // 16 rows at D=128, so those row offsets fold into immediate LDS offsets.
+  constexpr int KC_PERIOD = D == 64 ? 2 : 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5;
 
@@ -155,56 +141,100 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     return st;
   };
 
-  // Ring of NST stages, each one K tile and one V tile; the loads of step
-  // s + NST - 1 are in flight while step s computes.
-  auto bufK = [&](int s) -> TATTN_LDS char* { return smem + (s % NST) * 2 * TILE_BYTES; };
-  auto bufV = [&](int s) -> TATTN_LDS char* { return smem + (s % NST) * 2 * TILE_BYTES + TILE_BYTES; };
-  // Every step issues the same number of copies (ragged tails clamp their
-  // rows), so the vmcnt bookkeeping below is exact.
-  auto load_step = [&](int s) {
+  // ---- per-lane addresses, fixed for the whole tile ----
+  // Copies: lane slot (inst*64 + lane) of a tile is key row r, 16-byte chunk
+  // ch ^ swz(r); its global byte offset from the step's first key row is
+  // r * stride + 16 * chunk.
+  uint32_t dma_row[PER_WAVE], kvoff[PER_WAVE], vvoff[PER_WAVE], dma_lds[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;
+    const uint32_t slot = inst * 64 + lane;
+    const uint32_t row = slot / CPR;
+    const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
+    dma_row[i] = row;
+    kvoff[i] = (uint32_t)(row * p.k_sn + chunk * 8) * 2u;
+    vvoff[i] = (uint32_t)(row * p.v_sn + chunk * 8) * 2u;
+    dma_lds[i] = __builtin_amdgcn_readfirstlane(inst * 1024);
+    (void)chunk;
+  }
+  // S^T operand reads of K: row 32*kbk + lane%32, chunk 2c + lane/32.
+  uint32_t k_addr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) k_addr[c] = tile_off<D>(lane & 31, 2 * c + half);
+  // V^T operand reads (transposing): per 16-key chunk kc, d-block db and half e.
+  uint32_t v_addr[KC_PERIOD][NDB][2];
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < KC_PERIOD; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t row = 16 * kc + 4 * (g >> 1) + (j >> 2) + 8 * e;
+          const uint32_t dcol = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+          v_addr[kc][db][e] = tile_off<D>(row, dcol >> 3) + 8 * (j & 1);
+        }
+  }
+
+  // Loads of step s into ring stage `stage`.  Every step issues the same
+  // number of copies (a ragged tail clamps its rows to the last key), so the
+  // vmcnt bookkeeping in the loop is exact.
+  auto load_step = [&](int s, int stage) {
     int kb = step_at(s).kb;
-    kb = kb < 0 ? 0 : kb;
-    issue_tile_loads<D>(Kbh, Vbh, p.k_sn, p.v_sn, kb, p.Nk, bufK(s), bufV(s), wave, lane);
+    kb = kb < 0 ? 0 : (kb > p.Nk - 1 ? p.Nk - 1 : kb);
+    const uint32_t lk = lds_addr(smem) + stage * STAGE_BYTES;
+    const bf16* kbase = Kbh + (int64_t)kb * p.k_sn;
+    const bf16* vbase = Vbh + (int64_t)kb * p.v_sn;
+    if (kb + kKBlk <= p.Nk) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        dma16_sv(kbase, kvoff[i], lk + dma_lds[i]);
+        dma16_sv(vbase, vvoff[i], lk + TILE_BYTES + dma_lds[i]);
+      }
+    } else {
+      const uint32_t last = (uint32_t)(p.Nk - 1 - kb);
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const uint32_t over = dma_row[i] > last ? dma_row[i] - last : 0u;
+        dma16_sv(kbase, kvoff[i] - over * (uint32_t)p.k_sn * 2u, lk + dma_lds[i]);
+        dma16_sv(vbase, vvoff[i] - over * (uint32_t)p.v_sn * 2u, lk + TILE_BYTES + dma_lds[i]);
+      }
+    }
   };
-  constexpr int LOADS = 2 * (kKBlk * D / 8 / 64) / (kThreads / 64);  // copies per wave per step
 
   float m_run = kNegInf, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
 
-  if (p.Nk > 0) {
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < n_steps) load_step(s);
-  }
-  for (int s = 0; s < n_steps; ++s) {
-    // Loads issued after step s's: those of steps s+1 .. min(s+NST-2, n-1).
+  // One step of the ring at compile-time stage ST (so every LDS offset below
+  // is an immediate).
+  auto step = [&](auto stc, int s) {
+    constexpr int ST = decltype(stc)::value;
+    // Copies issued after step s's: those of steps s+1 .. min(s+NST-2, n-1).
     if constexpr (NST == 3) {
       if (s + 1 < n_steps) wait_vmem_le<LOADS>(); else wait_vmem();
-    } else if constexpr (NST == 4) {
-      if (s + 2 < n_steps) wait_vmem_le<2 * LOADS>();
-      else if (s + 1 < n_steps) wait_vmem_le<LOADS>();
-      else wait_vmem();
     } else {
+      static_assert(NST == 2, "ring depth");
       wait_vmem();
     }
     lds_barrier();
-    if (s + NST - 1 < n_steps) load_step(s + NST - 1);
+    if (s + NST - 1 < n_steps) load_step(s + NST - 1, (ST + NST - 1) % NST);
     const Step st = step_at(s);
-    if (st.kb < 0 || st.kb >= p.Nk) continue;  // second half of a ragged last tile
-    const TATTN_LDS char* tK = bufK(s);
-    const TATTN_LDS char* tV = bufV(s);
+    if (st.kb < 0 || st.kb >= p.Nk) return;  // second half of a ragged last tile
+    const TATTN_LDS char* tK = smem + ST * STAGE_BYTES;
+    const TATTN_LDS char* tV = tK + TILE_BYTES;
 
     // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks) ----
     f32x16 sacc[2];
 #pragma unroll
     for (int kbk = 0; kbk < 2; ++kbk) {
       sacc[kbk] = f32x16{};
-      const uint32_t row = 32 * kbk + (lane & 31);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8 kf = lds_read_b128(tK, tile_off<D>(row, 2 * c + half));
+        const bf16x8 kf = lds_read_b128(tK, k_addr[c] + kbk * 32 * 2 * D);
         sacc[kbk] = mfma32(kf, qf[c], sacc[kbk]);
       }
     }
@@ -254,19 +284,29 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     // ---- O^T += V^T P^T ----
-    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const uint32_t row0 = 16 * kc + 4 * (g >> 1) + (j >> 2);
+      constexpr int ROW_BYTES = 2 * D;
+      const uint32_t kc_off = (kc / KC_PERIOD) * (16 * KC_PERIOD) * ROW_BYTES;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint32_t dcol = 32 * db + 16 * (g & 1) + 4 * (j & 3);
-        const uint32_t sub = 8 * (j & 1);
-        const i16x4 v0 = lds_read_tr16(tV, tile_off<D>(row0, dcol >> 3) + sub);
-        const i16x4 v1 = lds_read_tr16(tV, tile_off<D>(row0 + 8, dcol >> 3) + sub);
+        const i16x4 v0 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][0] + kc_off);
+        const i16x4 v1 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][1] + kc_off);
         oacc[db] = mfma32(join_tr(v0, v1), pf[kc], oacc[db]);
       }
     }
+  };
+
+  if (p.Nk > 0) {
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < n_steps) load_step(s, s);
+  }
+  for (int s0 = 0; s0 < n_steps; s0 += NST) {
+    step(std::integral_constant<int, 0>{}, s0);
+    if (s0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, s0 + 1);
+    if constexpr (NST > 2)
+      if (s0 + 2 < n_steps) step(std::integral_constant<int, 2>{}, s0 + 2);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m ln2 + ln l ----
