@@ -162,6 +162,34 @@ def test_q0_lse_counts_exact(spec):
             assert np.max(np.abs(f64(o)[0, :, r] - vv[:, : r + 1].mean(1))) <= O_TOL
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["ramp", "spike", "overflow"])
+def test_score_range_moves_reference(kind, D):
+    """Scores far from N(0,1): rising key norms (the running max moves at most steps),
+    planted keys about 2^15 above the rest (base-2 units), and planted keys whose exp2
+    against the previous reference overflows fp32 (about 2^150).  Exercises every rescale
+    path of the online softmax."""
+    announce(f"score range {kind} D={D}")
+    N = 700
+    g = W.generator(11 + D)
+    q = W.randn_bf16(g, (1, 2, N, D)).float()
+    k = W.randn_bf16(g, (1, 2, N, D)).float()
+    v = W.randn_bf16(g, (1, 2, N, D))
+    if kind == "ramp":
+        k = k * torch.linspace(0.25, 6.0, N)[None, None, :, None]
+    else:
+        mult = 1.5 if kind == "spike" else 12.0
+        for j in (3, 150, 151, 420, 699):
+            k[:, :, j] = q[:, :, min(j + 40, N - 1)] * mult
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    for causal in (False, True):
+        gm, mod = _mask_pair({"causal": causal} if causal else {}, 1, N, N)
+        o, lse = _run(q, k, v, scale, gm)
+        ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
+        assert_close(f64(o), f64(lse), ro, rl, f"{kind} causal={causal}")
+
+
 def test_empty_key_sequence():
     announce("Nk = 0")
     q = torch.randn(1, 2, 70, 64).to(torch.bfloat16)

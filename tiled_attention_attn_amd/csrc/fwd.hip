@@ -36,7 +36,8 @@ namespace tattn {
 constexpr int kQTile = 128;
 constexpr int kKBlk = 64;
 constexpr int kThreads = 256;
-constexpr float kLazy = 8.0f;  // log2 headroom before the reference max moves
+// A lane's partial row sum of P (32 values) above 2^12 moves the reference max.
+constexpr float kSumCap = 4096.0f;
 
 // Pipeline depth (LDS stages) per head dim: 3 x 16 KB at D=64, 2 x 32 KB at
 // D=128, so two work groups fit in one CU's LDS.
@@ -204,7 +205,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
@@ -239,50 +240,71 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       }
     }
     // ---- mask (partial steps only) ----
+    // Element (kbk, r) holds key kb + 32 kbk + 8 (r/4) + 4 half + r%4; it is
+    // visible iff lo_m <= key <= hi_m, one unsigned compare of key - lo_m
+    // against hi_m - lo_m.  `sees`: the row has a visible key in this step.
+    bool sees = true;
     if (st.masked) {
       const int lo_m = st.use_row_interval ? lo : 0;
       const int hi_m = st.use_row_interval ? hi : p.Nk - 1;
+      sees = max(lo_m, st.kb) <= min(hi_m, min(st.kb + kKBlk, p.Nk) - 1);
+      const uint32_t base = (uint32_t)(st.kb + 4 * half - lo_m);
+      const uint32_t width = hi_m >= lo_m ? (uint32_t)(hi_m - lo_m) : 0u;
+      const uint32_t base_ok = hi_m >= lo_m ? base : 0x80000000u;
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = st.kb + 32 * kbk + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key < lo_m || key > hi_m) sacc[kbk][r] = kNegInf;
+          const uint32_t off = 32 * kbk + 8 * (r >> 2) + (r & 3);
+          if (base_ok + off > width) sacc[kbk][r] = kNegInf;
         }
     }
-    // ---- online softmax with a lazily moved reference max ----
-    // Probabilities are taken against m_run; m_run (and O, l) are only
-    // rescaled when some row's max exceeds it by more than 2^kLazy, so
-    // exp2(s - m_run) <= 2^kLazy stays well inside fp32 / bf16 range.
-    float mx = sacc[0][0];
+    // ---- online softmax against a lazily moved reference max ----
+    // P = exp2(c2 s - m_ref) is taken against the row's reference m_ref
+    // without a row max on the common path.  Every P value of a lane is at
+    // most that lane's partial row sum, so a partial sum <= 2^kSumCap proves
+    // them all in range.  Otherwise (a row max rose by about kSumCap, a
+    // non-finite score, or the first visible key of a row) the reference moves
+    // to the true row max, O and l are rescaled by exp2(m_old - m_new), and P
+    // is taken again.  Each row is thus normalised against some value at most
+    // kSumCap + log2(64) below its running max: the online softmax of
+    // section 3.2 with the rescale deferred until it is needed.
+    bf16x8 pf[4];
+    auto probs = [&](float m_use) -> float {
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+      for (int kc = 0; kc < 4; ++kc) {
+        float e[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-    mx = fmaxf(mx, other_half(mx)) * p.c2;
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
+        for (int i = 0; i < 8; ++i) {
+          e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
+          // l sums the fp32 values: summing the bf16-rounded P instead would
+          // put up to 2^-9 of relative error into LSE.
+          if (i & 1) ps1 += e[i]; else ps0 += e[i];
+        }
+        pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      }
+      return ps0 + ps1;
+    };
+    float psum = probs(m_ref == kNegInf ? 0.f : m_ref);
+    if (__any((m_ref == kNegInf && sees) || !(psum <= kSumCap))) {
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+      mx = fmaxf(mx, other_half(mx)) * p.c2;
+      const float m_new = fmaxf(m_ref, mx);
       // A row that has seen no key yet has O = 0 and l = 0: alpha must be 0
       // there, also when its m_new is still -inf (exp2(-inf - -inf) is NaN).
-      const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
+      const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+      psum = probs(m_ref == kNegInf ? 0.f : m_ref);
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
-        l_run += e[i];
-      }
-      pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-    }
+    l_run += psum;
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -325,12 +347,16 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       }
     if (p.lse != nullptr && half == 0)
       p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] =
-          l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : kNegInf;
+          l_tot > 0.f ? m_ref * kLn2 + logf(l_tot) : kNegInf;
   }
 }
 
+// Waves per SIMD: 3 work groups per CU at D=64 (131 VGPRs, 48 KB of LDS
+// each), 2 at D=128 (up to 234 VGPRs, 64 KB of LDS each).
+template <int D> struct Occ { static constexpr int value = D == 64 ? 3 : 2; };
+
 template <int D, bool BM>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<D>::value, Occ<D>::value)))
 fwd_kernel(const FwdParams p) {
   constexpr int NST = Stages<D>::value;
   __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * kKBlk * D * 2];
