@@ -1,7 +1,8 @@
 // Prefill: fused, IO-aware exact attention for gfx950.
 //
 // One work group of 4 waves owns a 128-row query tile (32 rows per wave) and
-// streams the visible keys through LDS in 64-key steps, as the tiled method
+// streams the visible keys through LDS in steps of 128 keys (D=64) or 64 keys
+// (D=128), as the tiled method
 // of "FlashAttention 2 principles and PyTorch practice" (sections 1 and 3.1)
 // describes: the Q block stays on chip, K/V blocks are loaded once per step,
 // and an online softmax (section 3.2: running max M and exp-sum L, the
@@ -34,14 +35,17 @@
 namespace tattn {
 
 constexpr int kQTile = 128;
-constexpr int kKBlk = 64;
+// Keys per step: 128 at D=64, 64 at D=128 (a K or V tile is 16 KB either
+// way).  Longer steps halve the per-step barrier, wait and copy-issue cost
+// per key; at D=128 the 128-key stage (64 KB) would not leave room for two.
+template <int D> struct KBlk { static constexpr int value = D == 64 ? 128 : 64; };
 constexpr int kThreads = 256;
 // A lane's partial row sum of P (32 values) above 2^12 moves the reference max.
 constexpr float kSumCap = 4096.0f;
 
-// Pipeline depth (LDS stages) per head dim: 3 x 16 KB at D=64, 2 x 32 KB at
-// D=128, so two work groups fit in one CU's LDS.
-template <int D> struct Stages { static constexpr int value = D == 64 ? 3 : 2; };
+// Pipeline depth: two 32 KB stages (K tile + V tile), so two work groups fit
+// in one CU's LDS.
+template <int D> struct Stages { static constexpr int value = 2; };
 
 // XOR swizzle of the 16-byte chunks of tile row r (see the header comment).
 template <int D> struct Swz;
@@ -66,13 +70,16 @@ struct Step {
 template <int D, bool BM, int NST>
 __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
                                              int b, int h, int kvh) {
+  constexpr int kKBlk = KBlk<D>::value;
+  constexpr int NKB = kKBlk / 32;              // 32-key blocks of S^T per step
+  constexpr int NKC = kKBlk / 16;              // 16-key chunks of the PV MFMA per step
+  constexpr int SPT = 128 / kKBlk;             // steps per 128-key BlockMask tile
   constexpr int TILE_BYTES = kKBlk * D * 2;
   constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K tile then V tile
   constexpr int NC = D / 16;                   // d-chunks of the QK MFMA
   constexpr int NDB = D / 32;                  // d-blocks of the PV MFMA
   constexpr int CPR = D / 8;                   // 16-byte chunks per key row
   constexpr int PER_WAVE = kKBlk * CPR / 64 / (kThreads / 64);  // copies per wave per tile
-  constexpr int LOADS = 2 * PER_WAVE;          // K + V copies per wave per step
   // The swizzle repeats every KC_PERIOD 16-row key chunks: 32 rows at D=64,
   // 16 rows at D=128, so those row offsets fold into immediate LDS offsets.
   constexpr int KC_PERIOD = D == 64 ? 2 : 1;
@@ -121,7 +128,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     const int bb = p.bm_B > 1 ? b : 0, hh = p.bm_H > 1 ? h : 0;
     bm_row = (bb * p.bm_H + hh) * p.n_qt + qt;
     nf = p.full_num[bm_row];
-    n_steps = 2 * (nf + p.part_num[bm_row]);
+    n_steps = SPT * (nf + p.part_num[bm_row]);
   }
   auto step_at = [&](int s) -> Step {
     Step st;
@@ -131,10 +138,10 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       st.masked = !full;
       st.use_row_interval = 1;
     } else {
-      const int t = s >> 1;
+      const int t = s / SPT;
       const int64_t base = (int64_t)bm_row * p.nKt;
       const int kt = t < nf ? p.full_idx[base + t] : p.part_idx[base + t - nf];
-      st.kb = kt * 128 + (s & 1) * kKBlk;
+      st.kb = kt * 128 + (s % SPT) * kKBlk;
       const bool partial = t >= nf;
       st.use_row_interval = partial;
       st.masked = partial || st.kb + kKBlk > p.Nk;
@@ -214,13 +221,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   // is an immediate).
   auto step = [&](auto stc, int s) {
     constexpr int ST = decltype(stc)::value;
-    // Copies issued after step s's: those of steps s+1 .. min(s+NST-2, n-1).
-    if constexpr (NST == 3) {
-      if (s + 1 < n_steps) wait_vmem_le<LOADS>(); else wait_vmem();
-    } else {
-      static_assert(NST == 2, "ring depth");
-      wait_vmem();
-    }
+    // Step s's copies are the only ones in flight (two-stage ring).
+    static_assert(NST == 2, "ring depth");
+    wait_vmem();
     lds_barrier();
     if (s + NST - 1 < n_steps) load_step(s + NST - 1, (ST + NST - 1) % NST);
     const Step st = step_at(s);
@@ -228,10 +231,10 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     const TATTN_LDS char* tK = smem + ST * STAGE_BYTES;
     const TATTN_LDS char* tV = tK + TILE_BYTES;
 
-    // ---- S^T = K Q^T for keys kb .. kb+63 (two 32-key blocks) ----
-    f32x16 sacc[2];
+    // ---- S^T = K Q^T for the step's keys, in 32-key blocks ----
+    f32x16 sacc[NKB];
 #pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk) {
+    for (int kbk = 0; kbk < NKB; ++kbk) {
       sacc[kbk] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -252,7 +255,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       const uint32_t width = hi_m >= lo_m ? (uint32_t)(hi_m - lo_m) : 0u;
       const uint32_t base_ok = hi_m >= lo_m ? base : 0x80000000u;
 #pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
+      for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t off = 32 * kbk + 8 * (r >> 2) + (r & 3);
@@ -269,11 +272,11 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     // is taken again.  Each row is thus normalised against some value at most
     // kSumCap + log2(64) below its running max: the online softmax of
     // section 3.2 with the rescale deferred until it is needed.
-    bf16x8 pf[4];
+    bf16x8 pf[NKC];
     auto probs = [&](float m_use) -> float {
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < NKC; ++kc) {
         float e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -290,9 +293,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     if (__any((m_ref == kNegInf && sees) || !(psum <= kSumCap))) {
       float mx = sacc[0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+      for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
       mx = fmaxf(mx, other_half(mx)) * p.c2;
       const float m_new = fmaxf(m_ref, mx);
       // A row that has seen no key yet has O = 0 and l = 0: alpha must be 0
@@ -307,7 +310,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     l_run += psum;
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
+    for (int kc = 0; kc < NKC; ++kc) {
       constexpr int ROW_BYTES = 2 * D;
       const uint32_t kc_off = (kc / KC_PERIOD) * (16 * KC_PERIOD) * ROW_BYTES;
 #pragma unroll
@@ -327,8 +330,6 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   for (int s0 = 0; s0 < n_steps; s0 += NST) {
     step(std::integral_constant<int, 0>{}, s0);
     if (s0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, s0 + 1);
-    if constexpr (NST > 2)
-      if (s0 + 2 < n_steps) step(std::integral_constant<int, 2>{}, s0 + 2);
   }
 
   // ---- epilogue: O = O_acc / l, LSE = m ln2 + ln l ----
@@ -351,15 +352,15 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   }
 }
 
-// Waves per SIMD: 3 work groups per CU at D=64 (131 VGPRs, 48 KB of LDS
-// each), 2 at D=128 (up to 234 VGPRs, 64 KB of LDS each).
-template <int D> struct Occ { static constexpr int value = D == 64 ? 3 : 2; };
+// Waves per SIMD: two work groups per CU (64 KB of LDS and up to 256 VGPRs
+// per wave each).
+template <int D> struct Occ { static constexpr int value = 2; };
 
 template <int D, bool BM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<D>::value, Occ<D>::value)))
 fwd_kernel(const FwdParams p) {
   constexpr int NST = Stages<D>::value;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * kKBlk * D * 2];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * KBlk<D>::value * D * 2];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.xcd_remap) {
