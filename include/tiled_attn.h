@@ -208,6 +208,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3],
 /* attn_decode_combine: O = sum_s exp(LSE_s - LSE) O_s with
  * LSE = log sum_s exp(LSE_s) (max-shifted); splits with LSE_s = -inf weigh 0.
  *   o   [B, Hq, Lq, D] bf16 (strides (b, h, n)); lse float [B, Hq, Lq] or NULL.
+ * o and ws_o must be 16-byte aligned (ATTN_ERR_ALIGN otherwise).
  */
 int attn_decode_combine(const float* ws_o, const float* ws_lse,
                         int B, int Hq, int Lq, int S, int D,

@@ -285,7 +285,7 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, i
   if ((long)B * Hq * Lq > 0x7fffffffL) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (S < 1 || S > 65536) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(o)) return ATTN_ERR_ALIGN;
+  if (!aligned16(o) || !aligned16(ws_o)) return ATTN_ERR_ALIGN;
   if (B == 0 || Hq == 0 || Lq == 0) return ATTN_OK;
   return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, static_cast<bf16*>(o), o_stride[0],
                         o_stride[1], o_stride[2], lse, stream);

@@ -247,13 +247,19 @@ decode_kernel(const DecParams p) {
 }
 
 // One wave per (sequence, head, query) row: LSE = log sum_s exp(LSE_s),
-// O = sum_s exp(LSE_s - LSE) O_s.
+// O = sum_s exp(LSE_s - LSE) O_s.  The row's S x D partial outputs are read
+// as float4s spread over the 64 lanes (lane i takes float4s i, i + 64, ...),
+// so all of a row's loads are in flight together; a lane's float4s share one
+// d-slice because D/4 divides 64, and the lanes holding the same d-slice are
+// summed with cross-lane adds at the end.
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       int n_rows, int Hq, int Lq, int S,
                                                       bf16* o, int64_t o_sb, int64_t o_sh,
                                                       int64_t o_sn, float* lse) {
+  constexpr int Q4 = D / 4;  // float4s per split row
+  static_assert(64 % Q4 == 0, "a lane's float4s must share one d-slice");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= n_rows) return;
@@ -266,20 +272,25 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   for (int s = lane; s < S; s += 64) tot += __expf(L[s] - m_use);
   for (int k = 32; k >= 1; k >>= 1) tot += __shfl_xor(tot, k, 64);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  constexpr int PER = D / 64;
-  float acc[PER];
+  const f32x4* O = reinterpret_cast<const f32x4*>(ws_o + (int64_t)row * S * D);
+  const int n4 = S * Q4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = lane; i < n4; i += 64) {
+    const float w = __expf(L[i / Q4] - m_use) * inv;  // L = -inf gives 0
+    acc += w * O[i];
+  }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  const float* O = ws_o + (int64_t)row * S * D;
-  for (int s = 0; s < S; ++s) {
-    const float w = __expf(L[s] - m_use) * inv;  // L[s] = -inf gives 0
+  for (int k = Q4; k < 64; k <<= 1) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += w * O[(int64_t)s * D + lane + 64 * i];
+    for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], k, 64);
   }
   const int t = row % Lq, bh = row / Lq, h = bh % Hq, b = bh / Hq;
-  bf16* dst = o + b * o_sb + h * o_sh + (int64_t)t * o_sn;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) dst[lane + 64 * i] = (bf16)acc[i];
+  if (lane < Q4) {
+    bf16* dst = o + b * o_sb + h * o_sh + (int64_t)t * o_sn + 4 * lane;
+    const bf16x2 lo2 = pack2(acc[0], acc[1]), hi2 = pack2(acc[2], acc[3]);
+    *reinterpret_cast<bf16x4*>(dst) = bf16x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+  }
   if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m_use + logf(tot) : kNegInf;
 }
 
