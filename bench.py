@@ -14,8 +14,9 @@ times, each on its own seeded synthetic inputs with inputs resident in HBM:
   B=1 H=32 N=8192 D=128, block-sparse GQA at N=32768), in TFLOP/s.
 
 Each kernel is timed with HIP events recorded on the stream it is launched on
-(torch's current stream, which the binding passes to the library); K timed
-launches after W warm-up launches, bracketed by synchronisation.  The CPU
+(torch's current stream, which the binding passes to the library) around K
+back-to-back launches after W warm-up launches, bracketed by synchronisation;
+the per-launch figure is that time / K.  The CPU
 baseline is the fp64 oracle timed on this host's cores over a bounded sample
 of the headline workload.  One JSON line is printed on stdout.
 """
@@ -57,27 +58,32 @@ def measured_traffic(key):
 
 
 def time_launches(fn, steps, warmup):
-    """Average per-launch kernel time (ms) from HIP events on the current stream,
-    and the wall time of the whole timed region (ms)."""
+    """Kernel time per launch (ms): HIP events recorded on the current stream
+    (the stream the binding launches on) around `steps` back-to-back launches,
+    divided by `steps`; plus the shortest single launch of a second, event-
+    bracketed pass (informational), and the wall time of the timed region."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     outer0 = torch.cuda.Event(enable_timing=True)
     outer1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     outer0.record(stream)
+    for _ in range(steps):
+        fn()
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    wall = outer0.elapsed_time(outer1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(steps, 10))]
     for a, b in ev:
         a.record(stream)
         fn()
         b.record(stream)
-    outer1.record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return sum(per) / len(per), min(per), outer0.elapsed_time(outer1)
+    best = min(a.elapsed_time(b) for a, b in ev)
+    return wall / steps, best, wall
 
 
 def causal_pairs(N):
@@ -186,8 +192,8 @@ def bench_decode(T, W, steps, warmup):
     c_avg, _, _ = time_launches(comb, steps, warmup)
     avg, best, wall = time_launches(both, steps, warmup)
     kv_bytes = float(B * Hkv * Nk * D * 2 * 2)
-    return dict(avg_ms=avg, min_ms=best, wall_ms=wall, splitkv_ms=s_avg, combine_ms=c_avg,
-                splits=S, kv_bytes=kv_bytes)
+    return dict(avg_ms=avg, min_ms=best, wall_ms=wall, splitkv_ms=s_avg, splitkv_min_ms=s_min,
+                combine_ms=c_avg, splits=S, kv_bytes=kv_bytes)
 
 
 def cpu_baseline(budget_s=12.0):
@@ -297,6 +303,7 @@ def main():
             "workload": "decode_b16h32kv8q16k32768d128", "value": round(gbs, 1), "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "us_per_step": round(dec["avg_ms"] * 1e3, 2),
             "splitkv_us": round(dec["splitkv_ms"] * 1e3, 2),
+            "splitkv_min_us": round(dec["splitkv_min_ms"] * 1e3, 2),
             "combine_us": round(dec["combine_ms"] * 1e3, 2), "num_splits": dec["splits"],
             "roofline": {"bound": "hbm", "achieved": round(s_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(s_gbs / PEAK_HBM_GBS, 4),

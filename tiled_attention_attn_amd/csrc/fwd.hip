@@ -365,14 +365,19 @@ fwd_kernel(const FwdParams p) {
   int unit = blockIdx.x;
   if (p.xcd_remap) {
     // work groups are dealt round-robin to the 8 XCDs: give each XCD a
-    // contiguous range of units (whole heads) so K/V stay in one L2.
+    // contiguous range of units (whole KV heads) so K/V stay in one L2.
     const int per = gridDim.x >> 3;
     unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   }
-  const int slot = unit % p.n_slots;
-  const int bh = unit / p.n_slots;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int kvh = h / p.G;
+  // unit = ((b * Hkv + kvh) * n_slots + slot) * G + g: the G query heads that
+  // share a KV head are adjacent, so the work groups of one query tile for
+  // all of them run together and read the same K/V tiles through L2.
+  const int g = unit % p.G;
+  int r = unit / p.G;
+  const int slot = r % p.n_slots;
+  r /= p.n_slots;
+  const int kvh = r % p.Hkv, b = r / p.Hkv;
+  const int h = kvh * p.G + g;
   process_tile<D, BM, NST>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
