@@ -142,6 +142,26 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return r;
 }
 
+// ---- K/V tiles in LDS --------------------------------------------------------
+// A tile is `rows` key rows of D bf16 (2D bytes each).  The 16-byte chunks of
+// row r are XOR-swizzled by Swz<D>::f(r), which keeps both the ds_read_b128
+// K-operand reads (one chunk of 32 consecutive rows per half-wave) and the
+// ds_read_b64_tr_b16 V-operand reads free of bank conflicts.  The pattern
+// repeats every 32 rows at D=64 and every 16 rows at D=128.
+template <int D> struct Swz;
+template <> struct Swz<64> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r >> 2) ^ (r << 1)) & 7u; }
+};
+template <> struct Swz<128> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r ^ (r << 2)) & 15u; }
+};
+
+// Byte offset of 16-byte chunk `chunk` of key row `row` in a tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
+  return row * (2 * D) + 16u * (chunk ^ Swz<D>::f(row));
+}
+
 // ---- mask ----------------------------------------------------------------------
 struct MaskParams {
   uint32_t flags;

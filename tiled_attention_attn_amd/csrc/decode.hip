@@ -6,10 +6,10 @@
 // (sequence, KV head, key split) and all the query rows that read that KV
 // head -- G query heads x Lq draft tokens, packed 16 rows per wave -- so
 // every K/V byte of the split is read from HBM exactly once.  Within the
-// split the keys stream through LDS in 64-key steps with the same online
-// softmax as the prefill (running max, exp-sum, rescaled accumulator), and
-// the split's normalised partial O_s and LSE_s go to an fp32 workspace.  The
-// combine kernel then merges the splits by their LSE.
+// split the keys stream through LDS in steps of 64 keys (D=64) or 32 keys
+// (D=128) with an online softmax (running max, exp-sum, rescaled
+// accumulator), and the split's normalised partial O_s and LSE_s go to an
+// fp32 workspace.  The combine kernel then merges the splits by their LSE.
 //
 // gfx950 mapping:
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
@@ -30,18 +30,6 @@ constexpr int kDecMaxSplitPages = 2048;  // block-table entries of one split, ke
 // group's LDS (no copy into LDS at 64 KB or above is relied on), and 64 KB of
 // ring plus the 8 KB page table lets two work groups share a CU.
 template <int D> struct DecKBlk { static constexpr int value = D == 64 ? 64 : 32; };
-
-template <int D> struct DSwz;
-template <> struct DSwz<64> {
-  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r >> 2) ^ (r << 1)) & 7u; }
-};
-template <> struct DSwz<128> {
-  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r ^ (r << 2)) & 15u; }
-};
-template <int D>
-__device__ __forceinline__ uint32_t dtile_off(uint32_t row, uint32_t chunk) {
-  return row * (2 * D) + 16u * (chunk ^ DSwz<D>::f(row));
-}
 
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
@@ -137,7 +125,7 @@ decode_kernel(const DecParams p) {
       const int inst = wave * PER_WAVE + i;
       const int slot = inst * 64 + lane;
       const uint32_t row = slot / CPR;
-      const uint32_t chunk = (slot % CPR) ^ DSwz<D>::f(row);
+      const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
       int key = kb + (int)row;
       key = key < k_end ? key : k_end - 1;
       int pidx = key / p.ps - page0;  // in [0, n_split_pages) for every issued step
@@ -178,7 +166,7 @@ decode_kernel(const DecParams p) {
       const uint32_t row = 16 * kb16 + col;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sacc[kb16] = mfma16(lds_read_b128(tK, dtile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
+        sacc[kb16] = mfma16(lds_read_b128(tK, tile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
     }
     const bool full = kb >= wlo && kb + kDecKBlk - 1 <= whi;
     if (!full) {
@@ -223,8 +211,8 @@ decode_kernel(const DecParams p) {
       for (int db = 0; db < NDB; ++db) {
         const uint32_t dcol = 16 * db + 4 * (col & 3);
         const uint32_t sub = 8 * (col & 1);
-        const i16x4 v0 = lds_read_tr16(tV, dtile_off<D>(r1, dcol >> 3) + sub);
-        const i16x4 v1 = lds_read_tr16(tV, dtile_off<D>(r2, dcol >> 3) + sub);
+        const i16x4 v0 = lds_read_tr16(tV, tile_off<D>(r1, dcol >> 3) + sub);
+        const i16x4 v1 = lds_read_tr16(tV, tile_off<D>(r2, dcol >> 3) + sub);
         oacc[db] = mfma16(join_tr(v0, v1), pf[kc], oacc[db]);
       }
     }

@@ -47,20 +47,6 @@ constexpr float kSumCap = 4096.0f;
 // in one CU's LDS.
 template <int D> struct Stages { static constexpr int value = 2; };
 
-// XOR swizzle of the 16-byte chunks of tile row r (see the header comment).
-template <int D> struct Swz;
-template <> struct Swz<64> {
-  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r >> 2) ^ (r << 1)) & 7u; }
-};
-template <> struct Swz<128> {
-  static __device__ __forceinline__ uint32_t f(uint32_t r) { return (r ^ (r << 2)) & 15u; }
-};
-
-template <int D>
-__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
-  return row * (2 * D) + 16u * (chunk ^ Swz<D>::f(row));
-}
-
 struct Step {
   int kb;      // first key of the step
   int masked;  // apply [lo_m, hi_m] per element
@@ -388,7 +374,12 @@ fwd_kernel(const FwdParams p) {
   }
 }
 
+int launch_fwd_pp(const FwdParams& p, int D, hipStream_t stream);
+
+// Dense masks at D=128 run on the two-group ping-pong kernel of fwd_pp.hip
+// (measured 5% faster there); D=64 and BlockMask lists run on fwd_kernel.
 int launch_fwd(const FwdParams& p, int D, bool blockmask, hipStream_t stream) {
+  if (!blockmask && D == 128) return launch_fwd_pp(p, D, stream);
   const long units = (long)p.B * p.Hq * p.n_slots;
   dim3 grid((unsigned)units), block(kThreads);
   if (D == 64) {
