@@ -73,6 +73,15 @@ SMALL = [
     ("block_diffusion_d64_bs5", 1, 1, 1, 333, 333, 64, {"block": 5}),
     ("causal_window_d64", 1, 2, 2, 640, 640, 64, {"causal": True, "window": (200, 0)}),
     ("nonsquare_window", 1, 2, 2, 64, 1000, 128, {"window": (300, 20)}),
+    # D=128 dense masks run on 256-row tiles of 8 waves: row counts one past a
+    # tile, a tile with one valid wave, windows that leave waves without keys
+    # in some steps, and Nq > Nk with fully masked rows.
+    ("causal_d128_n257", 1, 2, 2, 257, 257, 128, {"causal": True}),
+    ("causal_d128_n513_gqa", 1, 4, 2, 513, 513, 128, {"causal": True}),
+    ("window_d128_n700_w40", 1, 2, 2, 700, 700, 128, {"window": (40, 3)}),
+    ("block_diffusion_d128_q300_k600", 1, 2, 2, 300, 600, 128, {"block": 16}),
+    ("causal_d128_q600_k300", 1, 2, 1, 600, 300, 128, {"causal": True}),
+    ("docs_d128_many", 1, 2, 2, 1100, 1100, 128, {"docs": [[3, 97, 256, 1, 300, 443]]}),
 ]
 
 
