@@ -31,6 +31,23 @@ constexpr int kDecMaxSplitPages = 2048;  // block-table entries of one split, ke
 // ring plus the 8 KB page table lets two work groups share a CU.
 template <int D> struct DecKBlk { static constexpr int value = D == 64 ? 64 : 32; };
 
+// Chunk swizzle of the decode K/V tiles.  At D=128 the PV operand reads take
+// key rows 8m..8m+7 at chunk pairs {2d, 2d+1} across 32 lanes, so row r gets
+// ((r & 7) << 1) | (r >> 3 & 1): the 8 rows of a pair-of-groups then hit
+// distinct chunk pairs (free of bank conflicts), and rows 0..15 still take 16
+// distinct chunks for the K reads.  D=64 uses the prefill's swizzle.
+template <int D> struct DecSwz;
+template <> struct DecSwz<64> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return Swz<64>::f(r); }
+};
+template <> struct DecSwz<128> {
+  static __device__ __forceinline__ uint32_t f(uint32_t r) { return ((r & 7u) << 1) | ((r >> 3) & 1u); }
+};
+template <int D>
+__device__ __forceinline__ uint32_t dec_tile_off(uint32_t row, uint32_t chunk) {
+  return row * (2 * D) + 16u * (chunk ^ DecSwz<D>::f(row));
+}
+
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
 template <int D>
@@ -125,7 +142,7 @@ decode_kernel(const DecParams p) {
       const int inst = wave * PER_WAVE + i;
       const int slot = inst * 64 + lane;
       const uint32_t row = slot / CPR;
-      const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
+      const uint32_t chunk = (slot % CPR) ^ DecSwz<D>::f(row);
       int key = kb + (int)row;
       key = key < k_end ? key : k_end - 1;
       int pidx = key / p.ps - page0;  // in [0, n_split_pages) for every issued step
@@ -166,7 +183,7 @@ decode_kernel(const DecParams p) {
       const uint32_t row = 16 * kb16 + col;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sacc[kb16] = mfma16(lds_read_b128(tK, tile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
+        sacc[kb16] = mfma16(lds_read_b128(tK, dec_tile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
     }
     const bool full = kb >= wlo && kb + kDecKBlk - 1 <= whi;
     if (!full) {
@@ -211,8 +228,8 @@ decode_kernel(const DecParams p) {
       for (int db = 0; db < NDB; ++db) {
         const uint32_t dcol = 16 * db + 4 * (col & 3);
         const uint32_t sub = 8 * (col & 1);
-        const i16x4 v0 = lds_read_tr16(tV, tile_off<D>(r1, dcol >> 3) + sub);
-        const i16x4 v1 = lds_read_tr16(tV, tile_off<D>(r2, dcol >> 3) + sub);
+        const i16x4 v0 = lds_read_tr16(tV, dec_tile_off<D>(r1, dcol >> 3) + sub);
+        const i16x4 v1 = lds_read_tr16(tV, dec_tile_off<D>(r2, dcol >> 3) + sub);
         oacc[db] = mfma16(join_tr(v0, v1), pf[kc], oacc[db]);
       }
     }
