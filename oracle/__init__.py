@@ -25,13 +25,14 @@ Modules:
     paged      -- logical K/V gathered from a paged pool through a block table
     blockmask  -- tile classes (EMPTY / PARTIAL / FULL) from a dense mask, and
                   the compacted per-row tile lists
+    backward   -- dQ, dK, dV of the same definition (softmax Jacobian, chain rule)
 
 Every function is pinned by CPU tests (brute force on tiny inputs, torch's
 float64 CPU scaled_dot_product_attention, closed forms, invariants and
 identities); no function here is "parity unpinned".
 """
-from . import masks, core, paged, blockmask
+from . import masks, core, paged, blockmask, backward
 from .core import attention, attention_rows, combine, scores, masked_softmax
 
-__all__ = ["masks", "core", "paged", "blockmask", "attention", "attention_rows", "combine",
+__all__ = ["masks", "core", "paged", "blockmask", "backward", "attention", "attention_rows", "combine",
            "scores", "masked_softmax"]

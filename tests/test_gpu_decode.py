@@ -93,18 +93,42 @@ def test_paged_equals_contiguous_bitwise():
                            y.view(torch.int32) if y.dtype == torch.float32 else y.view(torch.int16))
 
 
-def test_window_mask_decode():
-    """Non-causal symmetric window over a paged cache (the draft-model call shape)."""
-    announce("decode window")
-    wl = W.paged_decode("win", 2, 4, 2, 8, 3000, 128, page_size=16, pool_pages=400, seed=4)
-    S = 4
+WINDOW_CASES = [
+    # (id, B, Hq, Hkv, Lq, Nk, seq_lens, S): the draft model's sliding-window
+    # call over a paged cache, grouped by where the sequence ends against the
+    # (2048, 2048) window.
+    ("mixed_b2", 2, 4, 2, 8, 3000, [3000, 3000], 4),
+    ("short", 2, 4, 2, 8, 40, [40, 9], 2),
+    ("single_stream", 1, 8, 2, 8, 2100, [2100], 3),
+    ("window_edge", 2, 4, 1, 8, 2064, [2056, 2057], 4),
+    ("beyond_window", 2, 4, 2, 8, 6000, [6000, 4500], 6),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_window_mask_decode(case):
+    """Non-causal symmetric window over a paged cache (the draft-model call shape);
+    beyond the window the first splits see no key and must get weight 0."""
+    name, B, Hq, Hkv, Lq, Nk, sl, S = case
+    announce(f"decode window {name}")
+    pages = (Nk + 15) // 16
+    wl = W.paged_decode("win" + name, B, Hq, Hkv, Lq, Nk, 128, page_size=16,
+                        pool_pages=B * pages + 5, seed=4 + len(name), seq_lens=sl)
     ws_o, ws_l, o, lse = _decode(wl, S, mask=T.Mask(window=(2048, 2048)))
     t = wl.tensors
-    for b in range(2):
-        kl = OP.gather(f64(t["k_pool"]), t["block_table"].numpy(), b, 3000)[None]
-        vl = OP.gather(f64(t["v_pool"]), t["block_table"].numpy(), b, 3000)[None]
-        ro, rl = oracle.attention(f64(t["q"])[b:b + 1], kl, vl, wl.scale, M.window(2048, 2048, 8, 3000))
-        assert_close(f64(o[b:b + 1]), f64(lse[b:b + 1]), ro, rl, f"window b{b}")
+    kp, vp, bt = f64(t["k_pool"]), f64(t["v_pool"]), t["block_table"].numpy()
+    C = 16 * math.ceil(pages / S)
+    for b in range(B):
+        kl = OP.gather(kp, bt, b, sl[b])[None]
+        vl = OP.gather(vp, bt, b, sl[b])[None]
+        qb = f64(t["q"])[b:b + 1]
+        ro, rl = oracle.attention(qb, kl, vl, wl.scale, M.window(2048, 2048, Lq, sl[b]))
+        assert_close(f64(o[b:b + 1]), f64(lse[b:b + 1]), ro, rl, f"window {name} b{b}")
+        for s in range(S):
+            po, pl = oracle.attention(qb, kl, vl, wl.scale,
+                                      M.and_(M.window(2048, 2048, Lq, sl[b]), M.key_range(s * C, (s + 1) * C)))
+            assert_close(f64(ws_o[b:b + 1, :, :, s]), f64(ws_l[b:b + 1, :, :, s]), po, pl,
+                         f"window {name} b{b} split{s}")
 
 
 def test_config5_decode_b16h32kv8q16k32768d128_sampled():

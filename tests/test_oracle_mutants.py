@@ -9,8 +9,9 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import core as OA, masks as M, paged as OP, blockmask as OB
+from oracle import core as OA, masks as M, paged as OP, blockmask as OB, backward as OBW
 import test_oracle_pins as P
+import test_oracle_backward as PB
 
 PINS = [
     lambda: [P.pin_brute(c) for c in P.BRUTE_CASES],
@@ -18,7 +19,7 @@ PINS = [
     P.pin_sdpa_decode_paged, P.pin_probs_sum_to_one, P.pin_constant_v, P.pin_one_visible_key,
     P.pin_q0_counts, P.pin_identities, P.pin_split_combine, P.pin_paged_equals_contiguous,
     P.pin_blockmask_classes, P.test_hand_worked_golden, P.test_brute_force_paged_two_splits,
-]
+] + PB.BWD_PINS
 
 
 def _caught():
@@ -112,6 +113,42 @@ def _attention_rows_kv_swapped(q, k, v, scale, mask_mod, b, hq, rows):
 
 
 _orig_rows = OA.attention_rows
+_orig_bwd_rows = OBW.bwd_rows
+
+
+def _softmax_grad_no_delta(p, dp):
+    return p * dp
+
+
+def _softmax_grad_delta_sign(p, dp):
+    return p * (dp + np.sum(p * dp, axis=-1, keepdims=True))
+
+
+def _bwd_rows_dk_unscaled(q, k, v, do, scale, mask_mod, b, hq, rows):
+    dq, dk, dv, p, ds = _orig_bwd_rows(q, k, v, do, scale, mask_mod, b, hq, rows)
+    return dq, dk / scale, dv, p, ds
+
+
+def _bwd_rows_dq_uses_v(q, k, v, do, scale, mask_mod, b, hq, rows):
+    dq, dk, dv, p, ds = _orig_bwd_rows(q, k, v, do, scale, mask_mod, b, hq, rows)
+    kvh = hq // (q.shape[1] // k.shape[1])
+    return scale * (ds @ np.asarray(v[b, kvh], dtype=np.float64)), dk, dv, p, ds
+
+
+def _bwd_rows_dv_from_o(q, k, v, do, scale, mask_mod, b, hq, rows):
+    dq, dk, dv, p, ds = _orig_bwd_rows(q, k, v, do, scale, mask_mod, b, hq, rows)
+    kvh = hq // (q.shape[1] // k.shape[1])
+    return dq, dk, p.T @ (p @ np.asarray(v[b, kvh], dtype=np.float64)), p, ds
+
+
+def _bwd_rows_gqa_modulo(q, k, v, do, scale, mask_mod, b, hq, rows):
+    Hkv = k.shape[1]
+    G = q.shape[1] // Hkv
+    kk = np.repeat(np.asarray(k)[:, [hq % Hkv]], Hkv, axis=1)
+    vv = np.repeat(np.asarray(v)[:, [hq % Hkv]], Hkv, axis=1)
+    kvh = hq // G
+    kk[:, kvh], vv[:, kvh] = np.asarray(k)[:, hq % Hkv], np.asarray(v)[:, hq % Hkv]
+    return _orig_bwd_rows(q, kk, vv, do, scale, mask_mod, b, hq, rows)
 
 MUTANTS = {
     "scale_dropped": (OA, "scores", _scores_no_scale),
@@ -126,6 +163,12 @@ MUTANTS = {
     "blockmask_full_tiles_masked": (M, "blockmask", _blockmask_full_masked),
     "gqa_modulo_mapping": (OA, "attention_rows", _attention_rows_gqa_modulo),
     "k_v_transposed": (OA, "attention_rows", _attention_rows_kv_swapped),
+    "bwd_delta_dropped": (OBW, "softmax_grad", _softmax_grad_no_delta),
+    "bwd_delta_sign": (OBW, "softmax_grad", _softmax_grad_delta_sign),
+    "bwd_dk_unscaled": (OBW, "bwd_rows", _bwd_rows_dk_unscaled),
+    "bwd_dq_uses_v": (OBW, "bwd_rows", _bwd_rows_dq_uses_v),
+    "bwd_dv_from_o": (OBW, "bwd_rows", _bwd_rows_dv_from_o),
+    "bwd_gqa_modulo_mapping": (OBW, "bwd_rows", _bwd_rows_gqa_modulo),
 }
 
 
