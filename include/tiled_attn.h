@@ -25,7 +25,8 @@
  *   B/H/N dimensions in memory is accepted, so both [B, H, N, D] and
  *   [B, N, H, D] layouts pass without a copy (FlashAttention 2 article,
  *   section 2).  Strides must be multiples of 8 elements and base pointers
- *   16-byte aligned; the sequence (n) strides of K and V stay below 2^25.
+ *   16-byte aligned; the sequence (n) strides of K and V (and, for attn_bwd,
+ *   of Q and dO) stay below 2^24.
  * - LSE is fp32 [B, Hq, Nq], contiguous, natural log, scale included.  A row
  *   that sees no key gets O = 0 and LSE = -inf.  LSE pointers may be NULL
  *   where noted (then it is not written).
@@ -222,6 +223,41 @@ size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits);
 /* A split count that fills the GPU: enough (sequence, KV head, split) work
  * groups for every compute unit, never more splits than pages. */
 int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
+
+/* ---- backward pass ---------------------------------------------------------
+ * Gradients of attn_fwd's O for an upstream gradient dO, by recomputation:
+ * only Q, K, V, O and the forward pass's LSE are read, and P is rebuilt tile
+ * by tile on chip (the segmented recomputation of the DeepSeek v2->v4
+ * attention article, section 2).  With P = exp(scale Q K^T + mask - LSE) and
+ * Delta = rowsum(dO * O):
+ *     dV = P^T dO,  dS = P * (dO V^T - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, o, d_o, dq   [B, Hq, Nq, D] bf16 (strides (b, h, n))
+ *   k, v, dk, dv    [B, Hkv, Nk, D] bf16
+ *   lse             float [B, Hq, Nq] contiguous, as attn_fwd wrote it
+ *                   (-inf for rows that see no key)
+ *   mask            the dense mask of the forward call (NULL = none)
+ *   workspace       device memory of at least attn_bwd_workspace_bytes(B, Hq,
+ *                   Nq) bytes, 16-byte aligned, overwritten (per-row Delta
+ *                   and LSE in base 2); may be NULL when Nq = 0
+ * dq, dk and dv are fully written: rows and keys that see nothing get 0.
+ * With GQA, dk / dv of a KV head sum the G query heads that read it (no
+ * atomics: one work group owns each key tile).  Outputs must not overlap the
+ * inputs or the workspace.  Nq or Nk may be 0; tensors without rows may then
+ * be NULL.  Three kernels run on `stream`, in order.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+int attn_bwd(const void* q, const int64_t q_stride[3],
+             const void* k, const int64_t k_stride[3],
+             const void* v, const int64_t v_stride[3],
+             const void* o, const int64_t o_stride[3],
+             const void* d_o, const int64_t do_stride[3], const float* lse,
+             void* dq, const int64_t dq_stride[3],
+             void* dk, const int64_t dk_stride[3],
+             void* dv, const int64_t dv_stride[3],
+             int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             const attn_mask_desc* mask, float* workspace, size_t workspace_bytes,
+             hipStream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_str(int status);

@@ -67,6 +67,7 @@ def test_fwd_argument_errors(T):
     assert _fwd(T, Hq=3, Hkv=2) == -4
     assert _fwd(T, Hkv=0) == -4
     assert _fwd(T, qs=(64 * 256, 64 * 256, 60)) == -5
+    assert _fwd(T, ks=(1 << 30, 1 << 30, 1 << 24)) == -5  # 128-row tiles, 32-bit offsets
     assert _fwd(T, q=18) == -6
     assert _fwd(T, Nq=-1) == -2
     assert _fwd(T, scale=0.0) == -11
@@ -122,6 +123,39 @@ def test_blockmask_and_decode_argument_errors(T):
     assert lib.attn_decode_num_splits(1, 300, 10000, 256) == 5  # at most 2048 pages per split
     assert dec(S=1, maxp=4097, bts=4097) == -8                  # 4097 pages in one split
     assert lib.attn_decode_ws_o_bytes(16, 32, 16, 128, 4) == 16 * 32 * 16 * 4 * 128 * 4
+
+
+def test_bwd_argument_errors(T):
+    lib = T.lib_handle()
+    qs = _strides(64 * 256, 64 * 256, 64)
+    ws = T.attn_bwd_workspace_bytes(1, 1, 256)
+    assert ws == 2 * 256 * 4 and T.attn_bwd_workspace_bytes(2, 3, 65) == 2 * 2 * 3 * 128 * 4
+
+    def bwd(**kw):
+        a = dict(q=16, k=32, v=48, o=64, do=80, lse=96, dq=112, dk=128, dv=144, s=qs, ks=qs, B=1, Hq=1,
+                 Hkv=1, Nq=256, Nk=256, D=64, scale=0.125, mask=None, ws=160, wsb=ws)
+        a.update(kw)
+        mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+        s, ks = a["s"], a["ks"]
+        return lib.attn_bwd(a["q"], s, a["k"], ks, a["v"], s, a["o"], s, a["do"], s, a["lse"], a["dq"], s,
+                            a["dk"], s, a["dv"], s, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
+                            a["scale"], mk, a["ws"], a["wsb"], None)
+    assert bwd(do=None) == -1
+    assert bwd(lse=None) == -1
+    assert bwd(dk=None) == -1
+    assert bwd(ws=None) == -1
+    assert bwd(D=32) == -3
+    assert bwd(Hq=2, Hkv=3) == -4
+    assert bwd(s=_strides(64 * 256, 64 * 256, 68)) == -5
+    assert bwd(ks=_strides(1 << 30, 1 << 30, 1 << 24)) == -5  # streamed row stride over 2^24
+    assert bwd(dv=150) == -6
+    assert bwd(scale=-1.0) == -11
+    assert bwd(mask=T.attn_mask_desc(flags=32)) == -7
+    assert bwd(wsb=ws - 4) == -8
+    assert bwd(B=0) == 0
+    # no rows and no keys: nothing to compute; row-less tensors may be NULL
+    assert bwd(Nq=0, Nk=0, q=None, o=None, do=None, dq=None, lse=None, ws=None, k=None, v=None,
+               dk=None, dv=None) == 0
 
 
 def test_product_path_does_not_reach_the_oracle():

@@ -186,3 +186,55 @@ BWD_PINS = [
     pin_bwd_autograd_causal_gqa, pin_bwd_autograd_window_docs, pin_bwd_autograd_block,
     pin_bwd_invariants, pin_bwd_gqa_equals_repeated,
 ]
+
+
+def test_bwd_bound_rejects_plausible_kernel_mistakes():
+    """The GPU bar |g - g_ref| <= 2^-7 m (m from ``bound=True``) must reject the mistakes a
+    tiled backward kernel could plausibly make: each mistaken gradient, computed here in
+    float64, exceeds the bar somewhere."""
+    N, D, G = 300, 64, 2
+    q, k, v = _tiny(41, 1, 2 * G, 2, N, N, D)
+    do = _rand(42, (1, 2 * G, N, D))
+    sc = 1.0 / math.sqrt(D)
+    mod = M.causal(N, N)
+    dq, dk, dv, (mq, mk, mv) = OBW.attention_bwd(q, k, v, do, sc, mod, bound=True)
+    tol = (2.0 ** -7) * np.asarray(mq), (2.0 ** -7) * np.asarray(mk), (2.0 ** -7) * np.asarray(mv)
+
+    def rejected(g, t):
+        return bool(np.any(np.abs(g[0] - g[1]) > t))
+
+    # a skipped 64-row step in dK / dV (rows 128..191 of every head)
+    skip = M.and_(mod, lambda b, h, qi, ki: ~((np.asarray(qi) >= 128) & (np.asarray(qi) < 192))
+                  & np.ones(np.broadcast(np.asarray(qi), np.asarray(ki)).shape, dtype=bool))
+    _, dk_s, dv_s = OBW.attention_bwd(q, k, v, do, sc, skip)
+    assert rejected((dk_s, dk), tol[1]) and rejected((dv_s, dv), tol[2])
+    # a skipped 128-key step in dQ (keys 0..127), everything else exact
+    dq_s = dq.copy()
+    for h in range(2 * G):
+        kvh = h // G
+        p = np.zeros((N, N))
+        s = sc * q[0, h] @ k[0, kvh].T
+        vis = np.tril(np.ones((N, N), dtype=bool))
+        s = np.where(vis, s, -np.inf)
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        dp = do[0, h] @ v[0, kvh].T
+        ds = OBW.softmax_grad(p, dp)
+        dq_s[0, h] -= sc * ds[:, :128] @ k[0, kvh, :128]
+    assert rejected((dq_s, dq), tol[0])
+    # GQA: dK / dV of a KV head from its first query head only
+    dq1, dk1, dv1 = OBW.attention_bwd(q[:, ::G], k, v, do[:, ::G], sc, mod)
+    assert rejected((dk1, dk), tol[1]) and rejected((dv1, dv), tol[2])
+    # dS without the rowsum term, and P taken with the neighbouring row's LSE
+    orig = OBW.softmax_grad
+    try:
+        OBW.softmax_grad = lambda p, dp: p * dp
+        dq2, dk2, _ = OBW.attention_bwd(q, k, v, do, sc, mod)
+        assert rejected((dq2, dq), tol[0]) and rejected((dk2, dk), tol[1])
+        OBW.softmax_grad = lambda p, dp: orig(np.roll(p, 1, axis=0) * p.sum(1, keepdims=True), dp)
+        dq3, dk3, dv3 = OBW.attention_bwd(q, k, v, do, sc, mod)
+        assert rejected((dq3, dq), tol[0]) and rejected((dk3, dk), tol[1])
+    finally:
+        OBW.softmax_grad = orig
+    # dK without the softmax scale
+    assert rejected((dk / sc, dk), tol[1])

@@ -74,6 +74,9 @@ def _load():
         "attn_decode_ws_o_bytes": (S, [I, I, I, I, I]),
         "attn_decode_ws_lse_bytes": (S, [I, I, I, I]),
         "attn_decode_num_splits": (I, [I, I, I, I]),
+        "attn_bwd": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
+                         I, I, I, I, I, I, F, MP, P, S, P]),
+        "attn_bwd_workspace_bytes": (S, [I, I, I]),
         "attn_status_str": (ctypes.c_char_p, [I]),
         "attn_abi_version": (I, []),
     }
@@ -87,8 +90,8 @@ def _load():
 _lib = _load()
 EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_blockmask_bytes",
            "attn_decode_splitkv", "attn_decode_combine", "attn_decode_ws_o_bytes",
-           "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_status_str",
-           "attn_abi_version")
+           "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_status_str", "attn_abi_version")
 
 
 def _check(func: str, status: int):
@@ -293,6 +296,35 @@ def attn_decode_combine(ws_o, ws_lse, o, lse=None, stream=None):
                                   _ptr(lse), _stream(stream))
     _check("attn_decode_combine", st)
     return o, lse
+
+
+def attn_bwd_workspace_bytes(B, Hq, Nq):
+    return int(_lib.attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=None, stream=None):
+    """dQ, dK, dV (bf16, written into dq / dk / dv) for q/o/d_o [B,Hq,Nq,D], k/v [B,Hkv,Nk,D]
+    and the forward pass's lse float [B,Hq,Nq]; ``workspace`` is a float32 CUDA tensor of at
+    least attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here if None)."""
+    _bf16(q, k, v, o, d_o, dq, dk, dv)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be contiguous float32 [B, Hq, Nq]")
+    need = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise TypeError("workspace must be contiguous float32")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    st = _lib.attn_bwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                       _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse),
+                       _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                       B, Hq, Hkv, Nq, Nk, D, scale, mp, _ptr(workspace), workspace.numel() * 4,
+                       _stream(stream))
+    _check("attn_bwd", st)
+    return dq, dk, dv
 
 
 def attn_status_str(status: int) -> str:

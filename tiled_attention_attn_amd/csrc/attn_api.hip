@@ -14,6 +14,7 @@ int launch_decode(const DecParams& p, int D, hipStream_t stream);
 int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
                    bf16* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
                    hipStream_t stream);
+int launch_bwd(const BwdParams& p, int D, hipStream_t stream);
 }  // namespace tattn
 
 using namespace tattn;
@@ -21,6 +22,7 @@ using namespace tattn;
 namespace {
 
 constexpr int kMaxLen = 1 << 28;  // keeps every key / row index and product in range
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;  // sequence stride of streamed tiles
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -74,8 +76,9 @@ int check_common(const void* q, const int64_t* qs, const void* k, const int64_t*
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
     return ATTN_ERR_ALIGN;
-  // The prefill kernel addresses a 64-row K/V tile with 32-bit byte offsets.
-  if (ks[2] >= (int64_t)1 << 25 || vs[2] >= (int64_t)1 << 25) return ATTN_ERR_STRIDE;
+  // The prefill kernels address a K/V tile of up to 128 rows with 32-bit
+  // byte offsets: 127 rows of 2^24 - 8 elements stay below 2^32 bytes.
+  if (ks[2] >= kMaxRowStride || vs[2] >= kMaxRowStride) return ATTN_ERR_STRIDE;
   return check_scale(scale);
 }
 
@@ -99,6 +102,11 @@ void fill_fwd(FwdParams& p, const void* q, const int64_t* qs, const void* k, con
   p.nKt = (Nk + 127) / 128;
 }
 
+bool causal_like(const MaskParams& m) {
+  return (m.flags & (ATTN_MASK_CAUSAL | ATTN_MASK_BLOCK_CAUSAL)) != 0 &&
+         !(m.flags & (ATTN_MASK_WINDOW | ATTN_MASK_DOCUMENT));
+}
+
 void set_slots(FwdParams& p, bool paired) {
   p.paired = paired && p.n_qt > 1;
   p.n_slots = p.paired ? (p.n_qt + 1) / 2 : p.n_qt;
@@ -110,7 +118,7 @@ void set_slots(FwdParams& p, bool paired) {
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -142,8 +150,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if (B == 0 || Nq == 0) return ATTN_OK;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
-  set_slots(p, (p.mask.flags & (ATTN_MASK_CAUSAL | ATTN_MASK_BLOCK_CAUSAL)) != 0 &&
-                   !(p.mask.flags & (ATTN_MASK_WINDOW | ATTN_MASK_DOCUMENT)));
+  set_slots(p, causal_like(p.mask));
   return launch_fwd(p, D, false, stream);
 }
 
@@ -289,6 +296,82 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, i
   if (B == 0 || Hq == 0 || Lq == 0) return ATTN_OK;
   return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, static_cast<bf16*>(o), o_stride[0],
                         o_stride[1], o_stride[2], lse, stream);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 0 || Hq < 0 || Nq < 0) return 0;
+  const size_t pad = ((size_t)Nq + 63) / 64 * 64;
+  return 2 * (size_t)B * Hq * pad * sizeof(float);
+}
+
+int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+             const void* v, const int64_t v_stride[3], const void* o, const int64_t o_stride[3],
+             const void* d_o, const int64_t do_stride[3], const float* lse, void* dq,
+             const int64_t dq_stride[3], void* dk, const int64_t dk_stride[3], void* dv,
+             const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
+             float scale, const attn_mask_desc* mask, float* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+  // Tensors without rows may be NULL (an empty tensor has no storage).
+  if (Nq > 0 && (!q || !o || !d_o || !dq || !lse)) return ATTN_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+  if (!workspace && Nq > 0) return ATTN_ERR_NULL;
+  const int64_t* all[8] = {q_stride, k_stride, v_stride, o_stride, do_stride, dq_stride, dk_stride,
+                           dv_stride};
+  int st;
+  for (const int64_t* s : all)
+    if ((st = check_strides(s))) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  const void* ptrs[9] = {q, k, v, o, d_o, dq, dk, dv, workspace};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTN_ERR_ALIGN;
+  // K / V tiles (dQ kernel) and Q / dO tiles (dK / dV kernel) are streamed
+  // with 32-bit byte offsets.
+  if (k_stride[2] >= kMaxRowStride || v_stride[2] >= kMaxRowStride ||
+      q_stride[2] >= kMaxRowStride || do_stride[2] >= kMaxRowStride)
+    return ATTN_ERR_STRIDE;
+  if ((st = check_scale(scale))) return st;
+  BwdParams p;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.v = static_cast<const bf16*>(v);
+  p.o = static_cast<const bf16*>(o);
+  p.dout = static_cast<const bf16*>(d_o);
+  p.lse = lse;
+  p.dq = static_cast<bf16*>(dq);
+  p.dk = static_cast<bf16*>(dk);
+  p.dv = static_cast<bf16*>(dv);
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
+  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
+  p.do_sb = do_stride[0]; p.do_sh = do_stride[1]; p.do_sn = do_stride[2];
+  p.dq_sb = dq_stride[0]; p.dq_sh = dq_stride[1]; p.dq_sn = dq_stride[2];
+  p.dk_sb = dk_stride[0]; p.dk_sh = dk_stride[1]; p.dk_sn = dk_stride[2];
+  p.dv_sb = dv_stride[0]; p.dv_sh = dv_stride[1]; p.dv_sn = dv_stride[2];
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.nq_pad = (Nq + 63) / 64 * 64;
+  p.c2 = scale * 1.4426950408889634f;
+  p.scale = scale;
+  p.ws_l2 = workspace;
+  p.ws_delta = workspace + (size_t)B * Hq * p.nq_pad;
+  // Causal-like masks give later query tiles more keys and earlier key tiles
+  // more rows: pair tile i with n-1-i in both kernels.
+  const bool pair = causal_like(p.mask);
+  p.n_kt = (Nk + 127) / 128;
+  p.kv_paired = pair && p.n_kt > 1;
+  p.kv_slots = p.kv_paired ? (p.n_kt + 1) / 2 : p.n_kt;
+  p.kv_xcd_remap = ((long)B * Hkv * p.kv_slots) % 8 == 0;
+  p.n_qt = (Nq + 127) / 128;
+  p.q_paired = pair && p.n_qt > 1;
+  p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
+  p.q_xcd_remap = ((long)B * Hq * p.q_slots) % 8 == 0;
+  return launch_bwd(p, D, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,609 @@
+// Backward pass: dQ, dK, dV of fused exact attention, by recomputation, for
+// gfx950.
+//
+// Only the inputs, O and the per-row LSE are kept from the forward pass; P is
+// rebuilt tile by tile from Q, K and the saved LSE whenever a gradient needs
+// it (the segmented recomputation of the DeepSeek v2->v4 attention article,
+// section 2; the N x N matrices never reach HBM, as in the forward tiling of
+// "FlashAttention 2 principles and PyTorch practice", sections 1 and 3.1).
+// With P = exp(scale QK^T + mask - LSE) and Delta = rowsum(dO * O):
+//
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),
+//     dQ = scale dS K,   dK = scale dS^T Q
+//
+// (rowsum(P * dP) = rowsum(dO * O) because O = P V, so Delta needs no pass
+// over the keys).  Three launches on the caller's stream:
+//
+//  * bwd_pre_kernel: Delta and L2 = LSE log2(e) per query row, into the
+//    caller's workspace (L2 = +inf for rows that see no key and for padding,
+//    so their P is 0).
+//  * bwd_kv_kernel: one work group per 128-key tile of one KV head; each wave
+//    keeps its 32 keys' K and V in registers and the G query heads' Q / dO
+//    tiles stream through LDS.  dK and dV of the KV head are summed over all
+//    G query heads in registers and written once: no atomics, deterministic.
+//  * bwd_q_kernel: one work group per 128-row query tile, shaped like the
+//    forward kernel (Q and dO in registers, K / V tiles through LDS); dQ is
+//    written once.
+//
+// gfx950 mapping (the operand layouts of the forward kernel):
+//  * kv kernel: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 with
+//    queries as M and the wave's keys as N, so each lane owns one key column.
+//    Those accumulators, converted to bf16, are directly the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS; the A operands dO^T and Q^T come from
+//    LDS with ds_read_b64_tr_b16, with the 16 queries of each MFMA permuted
+//    the same way as the accumulator rows.
+//  * q kernel: S^T = K Q^T and dP^T = V dO^T with keys as M, so each lane owns
+//    one query column and its L2 and Delta are scalars; dQ^T += K^T dS^T reads
+//    K^T with transposing LDS loads, as the forward reads V^T.
+//  * Masks: a query row's visible keys form an interval [lo, hi] whose ends
+//    never decrease with the row, so the rows that see a given key also form
+//    an interval [qa, qb]; the kv kernel finds it per lane by binary search
+//    over rows and tests each element with one unsigned compare.
+#include <type_traits>
+
+#include "params.h"
+
+namespace tattn {
+
+constexpr int kBwdThreads = 256;
+
+// ---- Delta and L2 per query row ----------------------------------------------
+// Eight lanes per row, 16-byte loads; rows of a (batch, head) padded to
+// nq_pad get Delta = 0 and L2 = +inf.
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) bwd_pre_kernel(const BwdParams p) {
+  const int64_t row = ((int64_t)blockIdx.x * kBwdThreads + threadIdx.x) >> 3;
+  const int j = threadIdx.x & 7;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.nq_pad;
+  if (row >= rows) return;  // whole 8-lane groups leave together
+  const int bh = (int)(row / p.nq_pad), qi = (int)(row % p.nq_pad);
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  float acc = 0.f;
+  if (qi < p.Nq) {
+    const bf16* orow = p.o + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
+    const bf16* drow = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)qi * p.do_sn;
+#pragma unroll
+    for (int c = j; c < D / 8; c += 8) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + 8 * c);
+      const bf16x8 d = *reinterpret_cast<const bf16x8*>(drow + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)a[i], (float)d[i], acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (j == 0) {
+    const float l = qi < p.Nq ? p.lse[(int64_t)bh * p.Nq + qi] : kNegInf;
+    p.ws_delta[row] = acc;
+    p.ws_l2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+  }
+}
+
+// Rows that see key `key`: [qa, qb] (empty when qa > qb).  hi(row) never
+// decreases, so {row : hi >= key} is a suffix of the rows; lo(row) never
+// decreases, so {row : lo <= key} is a prefix; the rows seeing the key are
+// their intersection.
+__device__ __forceinline__ void key_rows(const MaskParams& m, int b, int key, int Nq, int Nk,
+                                         int64_t shift, int& qa, int& qb) {
+  int a = 0, z = Nq;  // first row with hi >= key (Nq if none)
+  while (a < z) {
+    const int mid = (a + z) >> 1;
+    int l, h;
+    row_interval(m, b, mid + shift, Nk, l, h);
+    if (h >= key) z = mid; else a = mid + 1;
+  }
+  qa = a;
+  a = -1;
+  z = Nq - 1;  // last row with lo <= key (-1 if none)
+  while (a < z) {
+    const int mid = (a + z + 1) >> 1;
+    int l, h;
+    row_interval(m, b, mid + shift, Nk, l, h);
+    if (l <= key) a = mid; else z = mid - 1;
+  }
+  qb = a;
+}
+
+// Query rows per kv-kernel step: 64 at D=64, 32 at D=128 (a Q or dO tile is
+// 8 KB either way; a stage adds 1 KB for L2 and Delta).
+template <int D> struct BwdQRows { static constexpr int value = D == 64 ? 64 : 32; };
+
+template <int D>
+__device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem, int kt, int b,
+                                        int kvh) {
+  constexpr int QB = BwdQRows<D>::value;
+  constexpr int NQB = QB / 32;                  // 32-row blocks per step
+  constexpr int NC = D / 16;                    // d-chunks of the S / dP MFMAs
+  constexpr int NDB = D / 32;                   // d-blocks of the dK / dV MFMAs
+  constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  constexpr int TILE_BYTES = QB * D * 2;
+  constexpr int LD_OFF = 2 * TILE_BYTES;        // L2 then Delta, QB floats each
+  constexpr int STAGE_BYTES = LD_OFF + 1024;
+  constexpr int PER_WAVE = QB * CPR / 64 / (kBwdThreads / 64);
+  constexpr int ROW_BYTES = 2 * D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5;
+  const int64_t shift = (int64_t)p.Nk - p.Nq;
+
+  const int k0 = kt * 128;
+  const int key = k0 + wave * 32 + (lane & 31);
+  const bool key_ok = key < p.Nk;
+
+  // K and V of the lane's key: B operands of S = Q K^T and dP = dO V^T
+  // (k = head dim, n = key).
+  bf16x8 kf[NC], vf[NC];
+  {
+    const int r = key_ok ? key : p.Nk - 1;
+    const bf16* ks = p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)r * p.k_sn + 8 * half;
+    const bf16* vs = p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)r * p.v_sn + 8 * half;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = *reinterpret_cast<const bf16x8*>(ks + 16 * c);
+      vf[c] = *reinterpret_cast<const bf16x8*>(vs + 16 * c);
+    }
+    wait_vmem();
+  }
+
+  int qa = 0x3fffffff, qb = -1;
+  if (key_ok) key_rows(p.mask, b, key, p.Nq, p.Nk, shift, qa, qb);
+  if (qa > qb) { qa = 0x3fffffff; qb = -1; }
+  // Wave bounds: rows any lane sees [w_lo, w_hi]; rows every lane sees
+  // [w_lo_max, w_hi_min].
+  int w_lo = qa, w_hi = qb, w_lo_max = qa, w_hi_min = qb;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    w_lo = min(w_lo, __shfl_xor(w_lo, m, 64));
+    w_hi = max(w_hi, __shfl_xor(w_hi, m, 64));
+    w_lo_max = max(w_lo_max, __shfl_xor(w_lo_max, m, 64));
+    w_hi_min = min(w_hi_min, __shfl_xor(w_hi_min, m, 64));
+  }
+
+  // Rows the tile's keys see: from the first key's first row to the last
+  // key's last row (both ends never decrease with the key).
+  int n_qs = 0, qs0 = 0;
+  if (p.Nk > k0) {
+    int a0, b0, a1, b1;
+    key_rows(p.mask, b, k0, p.Nq, p.Nk, shift, a0, b0);
+    key_rows(p.mask, b, min(k0 + 127, p.Nk - 1), p.Nq, p.Nk, shift, a1, b1);
+    if (b1 >= a0) {
+      qs0 = (a0 / QB) * QB;
+      n_qs = (b1 + 1 - qs0 + QB - 1) / QB;
+    }
+  }
+  const int n_steps = p.G * n_qs;
+
+  // Copies: lane slot (inst*64 + lane) of a tile is row r, 16-byte chunk
+  // ch ^ swz(r), as for the forward kernel's K/V tiles.
+  uint32_t dma_row[PER_WAVE], qoff[PER_WAVE], dooff[PER_WAVE], dma_lds[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;
+    const uint32_t slot = inst * 64 + lane;
+    const uint32_t row = slot / CPR;
+    const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
+    dma_row[i] = row;
+    qoff[i] = (uint32_t)(row * p.q_sn + chunk * 8) * 2u;
+    dooff[i] = (uint32_t)(row * p.do_sn + chunk * 8) * 2u;
+    dma_lds[i] = __builtin_amdgcn_readfirstlane(inst * 1024);
+  }
+  // A-operand reads of Q and dO (row lane%32, chunk 2c + half) and the
+  // transposing reads of Q^T / dO^T per 16-row chunk kc, d-block db, half e.
+  uint32_t a_addr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) a_addr[c] = tile_off<D>(lane & 31, 2 * c + half);
+  uint32_t t_addr[2][NDB][2];
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t row = 16 * kc + 4 * (g >> 1) + (j >> 2) + 8 * e;
+          const uint32_t dcol = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+          t_addr[kc][db][e] = tile_off<D>(row, dcol >> 3) + 8 * (j & 1);
+        }
+  }
+
+  auto load_step = [&](int s, int stage) {
+    const int g = s / n_qs, qi = s - g * n_qs;
+    const int q0 = qs0 + qi * QB;
+    const int h = kvh * p.G + g;
+    const uint32_t lb = lds_addr(smem) + stage * STAGE_BYTES;
+    const bf16* qbase = p.q + b * p.q_sb + h * p.q_sh + (int64_t)q0 * p.q_sn;
+    const bf16* dbase = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)q0 * p.do_sn;
+    if (q0 + QB <= p.Nq) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        dma16_sv(qbase, qoff[i], lb + dma_lds[i]);
+        dma16_sv(dbase, dooff[i], lb + TILE_BYTES + dma_lds[i]);
+      }
+    } else {
+      // Rows past the end repeat the last row (their P is masked to 0).
+      const uint32_t last = (uint32_t)(p.Nq - 1 - q0);
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const uint32_t over = dma_row[i] > last ? dma_row[i] - last : 0u;
+        dma16_sv(qbase, qoff[i] - over * (uint32_t)p.q_sn * 2u, lb + dma_lds[i]);
+        dma16_sv(dbase, dooff[i] - over * (uint32_t)p.do_sn * 2u, lb + TILE_BYTES + dma_lds[i]);
+      }
+    }
+    if (wave == 0) {
+      // L2 (lanes 0 .. QB/4-1) then Delta (QB/4 .. QB/2-1), 16 bytes a lane;
+      // the other lanes repeat them into the stage's padding.  Rows up to
+      // q0 + QB lie inside the padded workspace row.
+      const int li = lane % (QB / 2);
+      const float* src = (li < QB / 4 ? p.ws_l2 : p.ws_delta) + (int64_t)(b * p.Hq + h) * p.nq_pad +
+                         q0 + 4 * (li % (QB / 4));
+      dma16(src, lb + LD_OFF);
+    }
+  };
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) dk[d] = dv[d] = f32x16{};
+
+  auto step = [&](auto stc, int s) {
+    constexpr int ST = decltype(stc)::value;
+    wait_vmem();
+    lds_barrier();
+    if (s + 1 < n_steps) load_step(s + 1, ST ^ 1);
+    const int g = s / n_qs, qi = s - g * n_qs;
+    const int q0 = qs0 + qi * QB;
+    if (q0 > w_hi || q0 + QB - 1 < w_lo) return;  // no key of this wave is seen by these rows
+    const bool full = w_lo_max <= q0 && w_hi_min >= q0 + QB - 1;
+    const TATTN_LDS char* tQ = smem + ST * STAGE_BYTES;
+    const TATTN_LDS char* tD = tQ + TILE_BYTES;
+    const TATTN_LDS float* tL = reinterpret_cast<const TATTN_LDS float*>(tQ + LD_OFF);
+#pragma unroll
+    for (int blk = 0; blk < NQB; ++blk) {
+      const int r0 = q0 + 32 * blk;
+      if (NQB > 1 && (r0 > w_hi || r0 + 31 < w_lo)) continue;
+      const uint32_t roff = blk * 32 * ROW_BYTES;
+      // ---- S = Q K^T and dP = dO V^T for 32 rows x the wave's 32 keys ----
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc = mfma32(lds_read_b128(tQ, a_addr[c] + roff), kf[c], sacc);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) dpacc = mfma32(lds_read_b128(tD, a_addr[c] + roff), vf[c], dpacc);
+      // Element r of the lane is row r0 + 8 (r/4) + 4 half + r%4: its L2 and
+      // Delta are four float4 broadcast reads each.
+      f32x4 l2[4], dl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l2[j] = *reinterpret_cast<const TATTN_LDS f32x4*>(tL + 32 * blk + 8 * j + 4 * half);
+        dl[j] = *reinterpret_cast<const TATTN_LDS f32x4*>(tL + QB + 32 * blk + 8 * j + 4 * half);
+      }
+      if (!full) {
+        const uint32_t base = (uint32_t)(r0 + 4 * half - qa);
+        const uint32_t width = qb >= qa ? (uint32_t)(qb - qa) : 0u;
+        const uint32_t base_ok = qb >= qa ? base : 0x80000000u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = 8 * (r >> 2) + (r & 3);
+          if (base_ok + off > width) sacc[r] = kNegInf;
+        }
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = fast_exp2(__builtin_fmaf(sacc[r], p.c2, -l2[r >> 2][r & 3]));
+        ds[r] = pr[r] * (dpacc[r] - dl[r >> 2][r & 3]);
+      }
+      bf16x8 pp[2], pd[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        pp[c] = pack8(pr[8 * c], pr[8 * c + 1], pr[8 * c + 2], pr[8 * c + 3], pr[8 * c + 4],
+                      pr[8 * c + 5], pr[8 * c + 6], pr[8 * c + 7]);
+        pd[c] = pack8(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3], ds[8 * c + 4],
+                      ds[8 * c + 5], ds[8 * c + 6], ds[8 * c + 7]);
+      }
+      // ---- dV^T += dO^T P and dK^T += Q^T dS over these 32 rows ----
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 a0 = lds_read_tr16(tD, t_addr[c][db][0] + roff);
+          const i16x4 a1 = lds_read_tr16(tD, t_addr[c][db][1] + roff);
+          dv[db] = mfma32(join_tr(a0, a1), pp[c], dv[db]);
+        }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 a0 = lds_read_tr16(tQ, t_addr[c][db][0] + roff);
+          const i16x4 a1 = lds_read_tr16(tQ, t_addr[c][db][1] + roff);
+          dk[db] = mfma32(join_tr(a0, a1), pd[c], dk[db]);
+        }
+    }
+  };
+
+  if (n_steps > 0) load_step(0, 0);
+  for (int s0 = 0; s0 < n_steps; s0 += 2) {
+    step(std::integral_constant<int, 0>{}, s0);
+    if (s0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, s0 + 1);
+  }
+
+  // ---- epilogue: lane owns key `key`, d = 32 db + 8 (r/4) + 4 half + r%4 ----
+  if (key_ok) {
+    bf16* dkrow = p.dk + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_sn;
+    bf16* dvrow = p.dv + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const bf16x2 a = pack2(dk[db][4 * r4] * p.scale, dk[db][4 * r4 + 1] * p.scale);
+        const bf16x2 c = pack2(dk[db][4 * r4 + 2] * p.scale, dk[db][4 * r4 + 3] * p.scale);
+        *reinterpret_cast<bf16x4*>(dkrow + 32 * db + 8 * r4 + 4 * half) = bf16x4{a[0], a[1], c[0], c[1]};
+        const bf16x2 e = pack2(dv[db][4 * r4], dv[db][4 * r4 + 1]);
+        const bf16x2 f = pack2(dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]);
+        *reinterpret_cast<bf16x4*>(dvrow + 32 * db + 8 * r4 + 4 * half) = bf16x4{e[0], e[1], f[0], f[1]};
+      }
+  }
+}
+
+// Waves per SIMD of the dK / dV kernel: at D=128 a wave holds 32 keys' K, V,
+// dK and dV (256 registers before any temporary), so it takes the whole
+// 512-entry register file of one SIMD lane.
+template <int D> struct BwdKvOcc { static constexpr int value = D == 64 ? 2 : 1; };
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads)
+__attribute__((amdgpu_waves_per_eu(BwdKvOcc<D>::value, BwdKvOcc<D>::value)))
+bwd_kv_kernel(const BwdParams p) {
+  constexpr int STAGE_BYTES = 2 * BwdQRows<D>::value * D * 2 + 1024;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
+  TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
+  int unit = blockIdx.x;
+  if (p.kv_xcd_remap) {
+    // whole KV heads per XCD, so their Q / dO tiles stay in one L2
+    const int per = gridDim.x >> 3;
+    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  const int slot = unit % p.kv_slots;
+  const int r = unit / p.kv_slots;
+  const int kvh = r % p.Hkv, b = r / p.Hkv;
+  kv_tile<D>(p, smem, slot, b, kvh);
+  if (p.kv_paired) {
+    const int kt2 = p.n_kt - 1 - slot;
+    if (kt2 != slot) {
+      __syncthreads();
+      kv_tile<D>(p, smem, kt2, b, kvh);
+    }
+  }
+}
+
+// ---- dQ -----------------------------------------------------------------------
+// Keys per step as in the forward kernel: 128 at D=64, 64 at D=128.
+template <int D> struct BwdKBlk { static constexpr int value = D == 64 ? 128 : 64; };
+
+template <int D>
+__device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem, int qt, int b,
+                                       int h, int kvh) {
+  constexpr int kKBlk = BwdKBlk<D>::value;
+  constexpr int NKB = kKBlk / 32;
+  constexpr int NC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int TILE_BYTES = kKBlk * D * 2;
+  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  constexpr int PER_WAVE = kKBlk * CPR / 64 / (kBwdThreads / 64);
+  constexpr int KC_PERIOD = D == 64 ? 2 : 1;  // 16-row chunks per swizzle period
+  constexpr int ROW_BYTES = 2 * D;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5;
+  const int64_t shift = (int64_t)p.Nk - p.Nq;
+
+  const int q0 = qt * 128;
+  const int qrow = q0 + wave * 32 + (lane & 31);
+  const bool row_ok = qrow < p.Nq;
+  const int rr = row_ok ? qrow : p.Nq - 1;
+
+  // Q^T and dO^T: B operands of S^T = K Q^T and dP^T = V dO^T.
+  bf16x8 qf[NC], df[NC];
+  float l2, dl;
+  {
+    const bf16* qs = p.q + b * p.q_sb + h * p.q_sh + (int64_t)rr * p.q_sn + 8 * half;
+    const bf16* ds = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)rr * p.do_sn + 8 * half;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = *reinterpret_cast<const bf16x8*>(qs + 16 * c);
+      df[c] = *reinterpret_cast<const bf16x8*>(ds + 16 * c);
+    }
+    const int64_t w = (int64_t)(b * p.Hq + h) * p.nq_pad + rr;
+    l2 = p.ws_l2[w];
+    dl = p.ws_delta[w];
+    wait_vmem();
+  }
+
+  int lo, hi;
+  row_interval(p.mask, b, qrow + shift, p.Nk, lo, hi);
+  int n_steps = 0, kb_begin = 0, lo_last = 0, hi_first = 0;
+  {
+    int lo_first, hi_last, t0;
+    const int last_row = min(q0 + 128, p.Nq) - 1;
+    row_interval(p.mask, b, q0 + shift, p.Nk, lo_first, hi_first);
+    row_interval(p.mask, b, last_row + shift, p.Nk, t0, hi_last);
+    lo_last = t0;
+    if (hi_last >= lo_first) {
+      kb_begin = (lo_first / kKBlk) * kKBlk;
+      n_steps = (hi_last + 1 - kb_begin + kKBlk - 1) / kKBlk;
+    }
+  }
+
+  uint32_t dma_row[PER_WAVE], kvoff[PER_WAVE], vvoff[PER_WAVE], dma_lds[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;
+    const uint32_t slot = inst * 64 + lane;
+    const uint32_t row = slot / CPR;
+    const uint32_t chunk = (slot % CPR) ^ Swz<D>::f(row);
+    dma_row[i] = row;
+    kvoff[i] = (uint32_t)(row * p.k_sn + chunk * 8) * 2u;
+    vvoff[i] = (uint32_t)(row * p.v_sn + chunk * 8) * 2u;
+    dma_lds[i] = __builtin_amdgcn_readfirstlane(inst * 1024);
+  }
+  uint32_t k_addr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) k_addr[c] = tile_off<D>(lane & 31, 2 * c + half);
+  uint32_t t_addr[KC_PERIOD][NDB][2];
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < KC_PERIOD; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t row = 16 * kc + 4 * (g >> 1) + (j >> 2) + 8 * e;
+          const uint32_t dcol = 32 * db + 16 * (g & 1) + 4 * (j & 3);
+          t_addr[kc][db][e] = tile_off<D>(row, dcol >> 3) + 8 * (j & 1);
+        }
+  }
+
+  const bf16* Kbh = p.k + b * p.k_sb + kvh * p.k_sh;
+  const bf16* Vbh = p.v + b * p.v_sb + kvh * p.v_sh;
+  auto load_step = [&](int s, int stage) {
+    const int kb = kb_begin + s * kKBlk;
+    const uint32_t lk = lds_addr(smem) + stage * STAGE_BYTES;
+    const bf16* kbase = Kbh + (int64_t)kb * p.k_sn;
+    const bf16* vbase = Vbh + (int64_t)kb * p.v_sn;
+    if (kb + kKBlk <= p.Nk) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        dma16_sv(kbase, kvoff[i], lk + dma_lds[i]);
+        dma16_sv(vbase, vvoff[i], lk + TILE_BYTES + dma_lds[i]);
+      }
+    } else {
+      const uint32_t last = (uint32_t)(p.Nk - 1 - kb);
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const uint32_t over = dma_row[i] > last ? dma_row[i] - last : 0u;
+        dma16_sv(kbase, kvoff[i] - over * (uint32_t)p.k_sn * 2u, lk + dma_lds[i]);
+        dma16_sv(vbase, vvoff[i] - over * (uint32_t)p.v_sn * 2u, lk + TILE_BYTES + dma_lds[i]);
+      }
+    }
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) dq[d] = f32x16{};
+
+  auto step = [&](auto stc, int s) {
+    constexpr int ST = decltype(stc)::value;
+    wait_vmem();
+    lds_barrier();
+    if (s + 1 < n_steps) load_step(s + 1, ST ^ 1);
+    const int kb = kb_begin + s * kKBlk;
+    const bool masked = !(kb >= lo_last && kb + kKBlk - 1 <= hi_first && kb + kKBlk <= p.Nk);
+    const TATTN_LDS char* tK = smem + ST * STAGE_BYTES;
+    const TATTN_LDS char* tV = tK + TILE_BYTES;
+    const uint32_t base = (uint32_t)(kb + 4 * half - lo);
+    const uint32_t width = hi >= lo ? (uint32_t)(hi - lo) : 0u;
+    const uint32_t base_ok = hi >= lo ? base : 0x80000000u;
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) {
+      // ---- S^T = K Q^T and dP^T = V dO^T for 32 keys ----
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sacc = mfma32(lds_read_b128(tK, k_addr[c] + kbk * 32 * ROW_BYTES), qf[c], sacc);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        dpacc = mfma32(lds_read_b128(tV, k_addr[c] + kbk * 32 * ROW_BYTES), df[c], dpacc);
+      // element r holds key kb + 32 kbk + 8 (r/4) + 4 half + r%4
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = 32 * kbk + 8 * (r >> 2) + (r & 3);
+          if (base_ok + off > width) sacc[r] = kNegInf;
+        }
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ds[r] = fast_exp2(__builtin_fmaf(sacc[r], p.c2, -l2)) * (dpacc[r] - dl);
+      // ---- dQ^T += K^T dS^T over these 32 keys (two 16-key chunks) ----
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pd = pack8(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3],
+                                ds[8 * c + 4], ds[8 * c + 5], ds[8 * c + 6], ds[8 * c + 7]);
+        const int kc = 2 * kbk + c;
+        const uint32_t kc_off = (kc / KC_PERIOD) * (16 * KC_PERIOD) * ROW_BYTES;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const i16x4 a0 = lds_read_tr16(tK, t_addr[kc % KC_PERIOD][db][0] + kc_off);
+          const i16x4 a1 = lds_read_tr16(tK, t_addr[kc % KC_PERIOD][db][1] + kc_off);
+          dq[db] = mfma32(join_tr(a0, a1), pd, dq[db]);
+        }
+      }
+    }
+  };
+
+  if (p.Nk > 0 && n_steps > 0) load_step(0, 0);
+  for (int s0 = 0; s0 < n_steps; s0 += 2) {
+    step(std::integral_constant<int, 0>{}, s0);
+    if (s0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, s0 + 1);
+  }
+
+  if (row_ok) {
+    bf16* drow = p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const bf16x2 a = pack2(dq[db][4 * r4] * p.scale, dq[db][4 * r4 + 1] * p.scale);
+        const bf16x2 c = pack2(dq[db][4 * r4 + 2] * p.scale, dq[db][4 * r4 + 3] * p.scale);
+        *reinterpret_cast<bf16x4*>(drow + 32 * db + 8 * r4 + 4 * half) = bf16x4{a[0], a[1], c[0], c[1]};
+      }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_q_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2];
+  TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
+  int unit = blockIdx.x;
+  if (p.q_xcd_remap) {
+    const int per = gridDim.x >> 3;
+    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  // unit = ((b * Hkv + kvh) * q_slots + slot) * G + g, as in the forward pass
+  const int g = unit % p.G;
+  int r = unit / p.G;
+  const int slot = r % p.q_slots;
+  r /= p.q_slots;
+  const int kvh = r % p.Hkv, b = r / p.Hkv;
+  const int h = kvh * p.G + g;
+  q_tile<D>(p, smem, slot, b, h, kvh);
+  if (p.q_paired) {
+    const int qt2 = p.n_qt - 1 - slot;
+    if (qt2 != slot) {
+      __syncthreads();
+      q_tile<D>(p, smem, qt2, b, h, kvh);
+    }
+  }
+}
+
+int launch_bwd(const BwdParams& p, int D, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.Hq * p.nq_pad;
+  const dim3 block(kBwdThreads);
+  const dim3 gpre((unsigned)((rows * 8 + kBwdThreads - 1) / kBwdThreads));
+  const dim3 gkv((unsigned)((int64_t)p.B * p.Hkv * p.kv_slots));
+  const dim3 gq((unsigned)((int64_t)p.B * p.Hq * p.q_slots));
+  if (D == 64) {
+    if (gpre.x) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, p);
+    if (gkv.x) hipLaunchKernelGGL(bwd_kv_kernel<64>, gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL(bwd_q_kernel<64>, gq, block, 0, stream, p);
+  } else {
+    if (gpre.x) hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, p);
+    if (gkv.x) hipLaunchKernelGGL(bwd_kv_kernel<128>, gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL(bwd_q_kernel<128>, gq, block, 0, stream, p);
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace tattn

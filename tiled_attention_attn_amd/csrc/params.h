@@ -60,4 +60,28 @@ struct DecParams {
   float* ws_lse;
 };
 
+// Backward pass (dQ, dK, dV by recomputation).
+struct BwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn, o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn, dq_sb, dq_sh, dq_sn, dk_sb, dk_sh, dk_sn, dv_sb, dv_sh, dv_sn;
+  int B, Hq, Hkv, G, Nq, Nk;
+  int nq_pad;  // workspace rows per (batch, head): Nq rounded up to 64
+  float c2;    // scale * log2(e)
+  float scale;
+  MaskParams mask;
+  float* ws_l2;     // [B*Hq][nq_pad]: LSE * log2(e); +inf for empty rows and padding
+  float* ws_delta;  // [B*Hq][nq_pad]: rowsum(dO * O); 0 for padding
+  int n_kt, kv_slots, kv_paired, kv_xcd_remap;  // 128-key tiles (dK / dV kernel)
+  int n_qt, q_slots, q_paired, q_xcd_remap;     // 128-row tiles (dQ kernel)
+};
+
 }  // namespace tattn
