@@ -11,7 +11,10 @@ times, each on its own seeded synthetic inputs with inputs resident in HBM:
   D=128, 16-token pages (splitkv + combine), KV-read GB/s = B*Hkv*Nk*D*2 bytes
   * 2 (K and V) / time, as a fraction of the 8 TB/s HBM peak;
 * the other prefill workloads (window+document and block-diffusion at
-  B=1 H=32 N=8192 D=128, block-sparse GQA at N=32768), in TFLOP/s.
+  B=1 H=32 N=8192 D=128, block-sparse GQA at N=32768), in TFLOP/s;
+* the backward pass (attn_bwd: dQ, dK, dV) on the causal headline shape and
+  on block-diffusion N=8192 D=128, in useful TFLOP/s (2.5x the forward's
+  FLOP: the five products S, dP, dV, dK, dQ).
 
 Each kernel is timed with HIP events recorded on the stream it is launched on
 (torch's current stream, which the binding passes to the library) around K
@@ -196,6 +199,42 @@ def bench_decode(T, W, steps, warmup):
                 combine_ms=c_avg, splits=S, kv_bytes=kv_bytes)
 
 
+def bench_backward(T, W, steps, warmup):
+    """attn_bwd (three kernels) on the causal 2x16x4096x64 workload and on block-diffusion
+    1x32x8192x128; upstream gradient dO is seeded N(0,1) bf16.  Useful FLOP = 2.5x the forward's
+    4 D (#visible pairs): the five products S, dP, dV, dK, dQ of 2 D per pair each."""
+    import numpy as np
+    import torch
+    out = []
+    for name in ("causal_b2h16n4096d64", "blockdiff_b1h32n8192d128"):
+        wl = W.FULL_SIZE[name]()
+        q, k, v = (wl.tensors[x].cuda() for x in ("q", "k", "v"))
+        B, H, N, D = q.shape
+        g = W.generator(77)
+        do = W.randn_bf16(g, tuple(q.shape)).cuda()
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+        if name.startswith("causal"):
+            mask = T.Mask(causal=True)
+            pairs = B * H * causal_pairs(N)
+        else:
+            mask = T.Mask(block_size=16)
+            p = np.arange(N)
+            pairs = B * H * visible_pairs_dense(np.zeros(N, dtype=np.int64),
+                                                np.minimum((p // 16 + 1) * 16 - 1, N - 1))
+        desc = mask.desc()
+        T.attn_fwd(q, k, v, o, lse, wl.scale, desc)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(T.attn_bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32, device="cuda")
+        fn = lambda: T.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, wl.scale, desc)
+        avg, best, wall = time_launches(fn, steps, warmup)
+        flops = 10.0 * D * pairs
+        out.append(dict(workload=name, avg_ms=avg, min_ms=best, tflops=flops / avg / 1e9,
+                        frac=flops / avg / 1e9 / PEAK_BF16_TFLOPS))
+        del q, k, v, o, lse, do, dq, dk, dv, ws
+    return out
+
+
 def cpu_baseline(budget_s=12.0):
     """The fp64 oracle on this host, on a bounded sample of the headline workload:
     whole (batch, head) slices of causal B=2 H=16 N=4096 D=64, in order, until the
@@ -241,7 +280,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline prefill only")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"], default="all",
                     help="profiling helper: run one kernel family only (copy = a plain "
                          "device-to-device copy of 1 GiB, for calibrating HBM counters)")
     args = ap.parse_args()
@@ -267,6 +306,11 @@ def main():
         dec = bench_decode(T, W, args.steps, args.warmup)
         log(f"decode: {dec['avg_ms']*1e3:.1f} us (splitkv {dec['splitkv_ms']*1e3:.1f} + combine "
             f"{dec['combine_ms']*1e3:.1f}), {dec['kv_bytes'] / dec['avg_ms'] / 1e6:.0f} GB/s")
+        return
+
+    if args.only == "backward":
+        for b in bench_backward(T, W, args.steps, args.warmup):
+            log(f"backward {b['workload']}: {b['avg_ms']*1e3:.1f} us, {b['tflops']:.1f} TFLOP/s")
         return
 
     wl, pf = bench_prefill_causal(T, W, args.steps, args.warmup)
@@ -316,6 +360,11 @@ def main():
             log(f"prefill {o['workload']}: {o['avg_ms']*1e3:.1f} us, {o['tflops']:.1f} TFLOP/s")
         result["prefill_other"] = [{k: (round(v, 4) if isinstance(v, float) else v)
                                     for k, v in o.items()} for o in others]
+        bwd = bench_backward(T, W, args.steps, args.warmup)
+        for b in bwd:
+            log(f"backward {b['workload']}: {b['avg_ms']*1e3:.1f} us, {b['tflops']:.1f} TFLOP/s")
+        result["backward"] = [{k: (round(v, 4) if isinstance(v, float) else v)
+                               for k, v in b.items()} for b in bwd]
     if not args.no_cpu_baseline:
         cb = cpu_baseline()
         log(f"cpu oracle: {cb['value']:.4f} TFLOP/s on {cb['cores']} threads ({cb['sample']})")
