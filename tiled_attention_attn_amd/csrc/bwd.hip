@@ -148,8 +148,8 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
   int qa = 0x3fffffff, qb = -1;
   if (key_ok) key_rows(p.mask, b, key, p.Nq, p.Nk, shift, qa, qb);
   if (qa > qb) { qa = 0x3fffffff; qb = -1; }
-  // Wave bounds: rows any lane sees [w_lo, w_hi]; rows every lane sees
-  // [w_lo_max, w_hi_min].
+  // Wave bounds, wave-uniform (scalar registers): rows any lane sees
+  // [w_lo, w_hi]; rows every lane sees [w_lo_max, w_hi_min].
   int w_lo = qa, w_hi = qb, w_lo_max = qa, w_hi_min = qb;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -158,6 +158,10 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
     w_lo_max = max(w_lo_max, __shfl_xor(w_lo_max, m, 64));
     w_hi_min = min(w_hi_min, __shfl_xor(w_hi_min, m, 64));
   }
+  w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+  w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+  w_lo_max = __builtin_amdgcn_readfirstlane(w_lo_max);
+  w_hi_min = __builtin_amdgcn_readfirstlane(w_hi_min);
 
   // Rows the tile's keys see: from the first key's first row to the last
   // key's last row (both ends never decrease with the key).
@@ -171,6 +175,8 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       n_qs = (b1 + 1 - qs0 + QB - 1) / QB;
     }
   }
+  n_qs = __builtin_amdgcn_readfirstlane(n_qs);
+  qs0 = __builtin_amdgcn_readfirstlane(qs0);
   const int n_steps = p.G * n_qs;
 
   // Copies: lane slot (inst*64 + lane) of a tile is row r, 16-byte chunk
@@ -207,13 +213,18 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
         }
   }
 
-  auto load_step = [&](int s, int stage) {
-    const int g = s / n_qs, qi = s - g * n_qs;
-    const int q0 = qs0 + qi * QB;
-    const int h = kvh * p.G + g;
+  // Steps run head-major: (g, qi) for g < G, qi < n_qs; a cursor per
+  // direction (copies issued, steps computed) advances without divisions.
+  const bf16* q_head = p.q + b * p.q_sb + (int64_t)kvh * p.G * p.q_sh;
+  const bf16* do_head = p.dout + b * p.do_sb + (int64_t)kvh * p.G * p.do_sh;
+  const float* ws_head = p.ws_l2 + (int64_t)(b * p.Hq + kvh * p.G) * p.nq_pad;
+  const int64_t ws_delta_off = p.ws_delta - p.ws_l2;
+  int ld_g = 0, ld_qi = 0;
+  auto load_next = [&](int stage) {
+    const int q0 = qs0 + ld_qi * QB;
     const uint32_t lb = lds_addr(smem) + stage * STAGE_BYTES;
-    const bf16* qbase = p.q + b * p.q_sb + h * p.q_sh + (int64_t)q0 * p.q_sn;
-    const bf16* dbase = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)q0 * p.do_sn;
+    const bf16* qbase = q_head + ld_g * p.q_sh + (int64_t)q0 * p.q_sn;
+    const bf16* dbase = do_head + ld_g * p.do_sh + (int64_t)q0 * p.do_sn;
     if (q0 + QB <= p.Nq) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -235,62 +246,78 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       // the other lanes repeat them into the stage's padding.  Rows up to
       // q0 + QB lie inside the padded workspace row.
       const int li = lane % (QB / 2);
-      const float* src = (li < QB / 4 ? p.ws_l2 : p.ws_delta) + (int64_t)(b * p.Hq + h) * p.nq_pad +
-                         q0 + 4 * (li % (QB / 4));
+      const float* src = ws_head + (int64_t)ld_g * p.nq_pad + (li < QB / 4 ? 0 : ws_delta_off) + q0 +
+                         4 * (li % (QB / 4));
       dma16(src, lb + LD_OFF);
     }
+    if (++ld_qi == n_qs) { ld_qi = 0; ++ld_g; }
   };
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) dk[d] = dv[d] = f32x16{};
 
+  int qi = 0;
   auto step = [&](auto stc, int s) {
     constexpr int ST = decltype(stc)::value;
     wait_vmem();
     lds_barrier();
-    if (s + 1 < n_steps) load_step(s + 1, ST ^ 1);
-    const int g = s / n_qs, qi = s - g * n_qs;
+    if (s + 1 < n_steps) load_next(ST ^ 1);
     const int q0 = qs0 + qi * QB;
+    if (++qi == n_qs) qi = 0;
     if (q0 > w_hi || q0 + QB - 1 < w_lo) return;  // no key of this wave is seen by these rows
     const bool full = w_lo_max <= q0 && w_hi_min >= q0 + QB - 1;
     const TATTN_LDS char* tQ = smem + ST * STAGE_BYTES;
     const TATTN_LDS char* tD = tQ + TILE_BYTES;
     const TATTN_LDS float* tL = reinterpret_cast<const TATTN_LDS float*>(tQ + LD_OFF);
+    // ---- S = Q K^T and dP = dO V^T for every 32-row block of the step ----
+    f32x16 sacc[NQB], dpacc[NQB];
 #pragma unroll
     for (int blk = 0; blk < NQB; ++blk) {
-      const int r0 = q0 + 32 * blk;
-      if (NQB > 1 && (r0 > w_hi || r0 + 31 < w_lo)) continue;
       const uint32_t roff = blk * 32 * ROW_BYTES;
-      // ---- S = Q K^T and dP = dO V^T for 32 rows x the wave's 32 keys ----
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      sacc[blk] = dpacc[blk] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc = mfma32(lds_read_b128(tQ, a_addr[c] + roff), kf[c], sacc);
+      for (int c = 0; c < NC; ++c) {
+        sacc[blk] = mfma32(lds_read_b128(tQ, a_addr[c] + roff), kf[c], sacc[blk]);
+        dpacc[blk] = mfma32(lds_read_b128(tD, a_addr[c] + roff), vf[c], dpacc[blk]);
+      }
+    }
+    // Keep the operand reads about four MFMAs ahead of their use.
+    constexpr int NSD = 2 * NQB * NC;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) dpacc = mfma32(lds_read_b128(tD, a_addr[c] + roff), vf[c], dpacc);
-      // Element r of the lane is row r0 + 8 (r/4) + 4 half + r%4: its L2 and
-      // Delta are four float4 broadcast reads each.
+    for (int i = 0; i < NSD - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if (!full) {
+      // element r of block blk is row q0 + 32 blk + 8 (r/4) + 4 half + r%4
+      const uint32_t width = qb >= qa ? (uint32_t)(qb - qa) : 0u;
+      const uint32_t base = qb >= qa ? (uint32_t)(q0 + 4 * half - qa) : 0x80000000u;
+#pragma unroll
+      for (int blk = 0; blk < NQB; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = 32 * blk + 8 * (r >> 2) + (r & 3);
+          if (base + off > width) sacc[blk][r] = kNegInf;
+        }
+    }
+#pragma unroll
+    for (int blk = 0; blk < NQB; ++blk) {
+      const uint32_t roff = blk * 32 * ROW_BYTES;
+      // Its L2 and Delta: four float4 broadcast reads each.
       f32x4 l2[4], dl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         l2[j] = *reinterpret_cast<const TATTN_LDS f32x4*>(tL + 32 * blk + 8 * j + 4 * half);
         dl[j] = *reinterpret_cast<const TATTN_LDS f32x4*>(tL + QB + 32 * blk + 8 * j + 4 * half);
       }
-      if (!full) {
-        const uint32_t base = (uint32_t)(r0 + 4 * half - qa);
-        const uint32_t width = qb >= qa ? (uint32_t)(qb - qa) : 0u;
-        const uint32_t base_ok = qb >= qa ? base : 0x80000000u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t off = 8 * (r >> 2) + (r & 3);
-          if (base_ok + off > width) sacc[r] = kNegInf;
-        }
-      }
       float pr[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pr[r] = fast_exp2(__builtin_fmaf(sacc[r], p.c2, -l2[r >> 2][r & 3]));
-        ds[r] = pr[r] * (dpacc[r] - dl[r >> 2][r & 3]);
+        pr[r] = fast_exp2(__builtin_fmaf(sacc[blk][r], p.c2, -l2[r >> 2][r & 3]));
+        ds[r] = pr[r] * (dpacc[blk][r] - dl[r >> 2][r & 3]);
       }
       bf16x8 pp[2], pd[2];
 #pragma unroll
@@ -308,19 +335,14 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
           const i16x4 a0 = lds_read_tr16(tD, t_addr[c][db][0] + roff);
           const i16x4 a1 = lds_read_tr16(tD, t_addr[c][db][1] + roff);
           dv[db] = mfma32(join_tr(a0, a1), pp[c], dv[db]);
-        }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const i16x4 a0 = lds_read_tr16(tQ, t_addr[c][db][0] + roff);
-          const i16x4 a1 = lds_read_tr16(tQ, t_addr[c][db][1] + roff);
-          dk[db] = mfma32(join_tr(a0, a1), pd[c], dk[db]);
+          const i16x4 b0 = lds_read_tr16(tQ, t_addr[c][db][0] + roff);
+          const i16x4 b1 = lds_read_tr16(tQ, t_addr[c][db][1] + roff);
+          dk[db] = mfma32(join_tr(b0, b1), pd[c], dk[db]);
         }
     }
   };
 
-  if (n_steps > 0) load_step(0, 0);
+  if (n_steps > 0) load_next(0);
   for (int s0 = 0; s0 < n_steps; s0 += 2) {
     step(std::integral_constant<int, 0>{}, s0);
     if (s0 + 1 < n_steps) step(std::integral_constant<int, 1>{}, s0 + 1);
