@@ -334,7 +334,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd_kernel<64,false>/causal_b2h16n4096d64"),
-                     "traffic_unit": "bytes/launch", "kernel": "fwd_kernel<64,false>",
+                     "traffic_unit": "bytes/launch", "kernel": "fwd_kernel<64, false, __bf16>",
                      "kernel_us": round(pf["avg_ms"] * 1e3, 2)},
     }
     if not args.quick and args.only == "all":
@@ -352,7 +352,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(s_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(s_gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_kernel<128>/decode_b16h32kv8q16k32768d128"),
-                         "traffic_unit": "bytes/launch", "kernel": "decode_kernel<128>"},
+                         "traffic_unit": "bytes/launch", "kernel": "decode_kernel<128, __bf16>"},
         }
     if not args.quick:
         others = bench_prefill_others(T, W, args.steps, args.warmup)

@@ -18,8 +18,11 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Q, K, V, O are bfloat16 (the kernel dtype the FlashAttention 2 article,
- *   section 7, asks for; fp32 callers convert first).  Accumulation is fp32.
+ * - Q, K, V, O (and dO, dQ, dK, dV) are 16-bit floats of one type, named by
+ *   the `dtype` argument: ATTN_DTYPE_BF16 or ATTN_DTYPE_F16 (the two kernel
+ *   dtypes the FlashAttention 2 article, section 7, allows; fp32 callers
+ *   convert first).  P is rounded to the same type for the P V product.
+ *   Accumulation is fp32.
  * - Tensors are logical [B, H, N, D] with D contiguous (stride 1).  Each
  *   tensor comes with three element strides for (b, h, n); any order of the
  *   B/H/N dimensions in memory is accepted, so both [B, H, N, D] and
@@ -67,6 +70,11 @@ extern "C" {
 #define ATTN_ERR_LAUNCH (-9)    /* the HIP runtime reported a launch error     */
 #define ATTN_ERR_BLOCKMASK (-10)/* BlockMask descriptor inconsistent           */
 #define ATTN_ERR_SCALE (-11)    /* scale not finite and > 0                    */
+#define ATTN_ERR_DTYPE (-12)    /* dtype is not ATTN_DTYPE_BF16 / ATTN_DTYPE_F16 */
+
+/* ---- element types ------------------------------------------------------ */
+#define ATTN_DTYPE_BF16 0
+#define ATTN_DTYPE_F16 1
 
 /* ---- masks --------------------------------------------------------------
  * A query row q is placed at the absolute position p = q + (Nk - Nq)
@@ -114,7 +122,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3],
              const void* k, const int64_t k_stride[3],
              const void* v, const int64_t v_stride[3],
              void* o, const int64_t o_stride[3], float* lse,
-             int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
              const attn_mask_desc* mask, hipStream_t stream);
 
 /* ---- BlockMask -----------------------------------------------------------
@@ -166,7 +174,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3],
                        const void* k, const int64_t k_stride[3],
                        const void* v, const int64_t v_stride[3],
                        void* o, const int64_t o_stride[3], float* lse,
-                       int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
                        const attn_mask_desc* mask, const attn_blockmask* bm,
                        hipStream_t stream);
 
@@ -177,8 +185,8 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3],
  *
  * attn_decode_splitkv: for each sequence b, KV head, split s and query row,
  * the attention over split s's keys only, normalised, in fp32:
- *   q           [B, Hq, Lq, D] bf16 (strides (b, h, n))
- *   k_cache,    [num_pages, page_size, Hkv, D] bf16, contiguous pool
+ *   q           [B, Hq, Lq, D] of `dtype` (strides (b, h, n))
+ *   k_cache,    [num_pages, page_size, Hkv, D] of `dtype`, contiguous pool
  *   v_cache
  *   block_table device int32 [B][bt_stride]; logical key j of sequence b
  *               lives in page block_table[b][j / page_size], slot j % page_size
@@ -202,17 +210,17 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3],
                         const void* k_cache, const void* v_cache, int64_t num_pages,
                         const int32_t* block_table, int64_t bt_stride,
                         const int32_t* seq_lens, int max_pages,
-                        int B, int Hq, int Hkv, int Lq, int D, int page_size,
+                        int B, int Hq, int Hkv, int Lq, int D, int dtype, int page_size,
                         int num_splits, float scale, const attn_mask_desc* mask,
                         float* ws_o, float* ws_lse, hipStream_t stream);
 
 /* attn_decode_combine: O = sum_s exp(LSE_s - LSE) O_s with
  * LSE = log sum_s exp(LSE_s) (max-shifted); splits with LSE_s = -inf weigh 0.
- *   o   [B, Hq, Lq, D] bf16 (strides (b, h, n)); lse float [B, Hq, Lq] or NULL.
+ *   o   [B, Hq, Lq, D] of `dtype` (strides (b, h, n)); lse float [B, Hq, Lq] or NULL.
  * o and ws_o must be 16-byte aligned (ATTN_ERR_ALIGN otherwise).
  */
 int attn_decode_combine(const float* ws_o, const float* ws_lse,
-                        int B, int Hq, int Lq, int S, int D,
+                        int B, int Hq, int Lq, int S, int D, int dtype,
                         void* o, const int64_t o_stride[3], float* lse,
                         hipStream_t stream);
 
@@ -231,8 +239,8 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
  * attention article, section 2).  With P = exp(scale Q K^T + mask - LSE) and
  * Delta = rowsum(dO * O):
  *     dV = P^T dO,  dS = P * (dO V^T - Delta),  dQ = scale dS K,  dK = scale dS^T Q.
- *   q, o, d_o, dq   [B, Hq, Nq, D] bf16 (strides (b, h, n))
- *   k, v, dk, dv    [B, Hkv, Nk, D] bf16
+ *   q, o, d_o, dq   [B, Hq, Nq, D] of `dtype` (strides (b, h, n))
+ *   k, v, dk, dv    [B, Hkv, Nk, D] of `dtype`
  *   lse             float [B, Hq, Nq] contiguous, as attn_fwd wrote it
  *                   (-inf for rows that see no key)
  *   mask            the dense mask of the forward call (NULL = none)
@@ -255,7 +263,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3],
              void* dq, const int64_t dq_stride[3],
              void* dk, const int64_t dk_stride[3],
              void* dv, const int64_t dv_stride[3],
-             int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
              const attn_mask_desc* mask, float* workspace, size_t workspace_bytes,
              hipStream_t stream);
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(T):
 
 def test_status_strings(T):
     assert T.attn_status_str(0) == "ok"
-    for code in range(-11, 0):
+    for code in range(-12, 0):
         assert T.attn_status_str(code) != "unknown status"
     assert T.attn_abi_version() >= 1
 
@@ -51,12 +51,13 @@ def _strides(*v):
 def _fwd(T, **kw):
     lib = T.lib_handle()
     a = dict(q=16, k=32, v=48, o=64, qs=(64 * 256, 64 * 256, 64), ks=None, vs=None, os=None, lse=None,
-             B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, scale=0.125, mask=None)
+             B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, dtype=0, scale=0.125, mask=None)
     a.update(kw)
     s = lambda x: _strides(*(x or a["qs"]))
     mk = None if a["mask"] is None else ctypes.byref(a["mask"])
     return lib.attn_fwd(a["q"], s(a["qs"]), a["k"], s(a["ks"]), a["v"], s(a["vs"]), a["o"], s(a["os"]),
-                        a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["scale"], mk, None)
+                        a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["dtype"], a["scale"],
+                        mk, None)
 
 
 def test_fwd_argument_errors(T):
@@ -64,6 +65,7 @@ def test_fwd_argument_errors(T):
     assert _fwd(T, q=None) == -1
     assert _fwd(T, k=None) == -1
     assert _fwd(T, D=96) == -3
+    assert _fwd(T, dtype=2) == -12 and _fwd(T, dtype=-1) == -12
     assert _fwd(T, Hq=3, Hkv=2) == -4
     assert _fwd(T, Hkv=0) == -4
     assert _fwd(T, qs=(64 * 256, 64 * 256, 60)) == -5
@@ -100,24 +102,27 @@ def test_blockmask_and_decode_argument_errors(T):
     assert lib.attn_blockmask_bytes(1, 1, 2, 2) == 2 * 4 * 2 + 2 * 2 * 4 * 2
     qs = _strides(32 * 16 * 128, 16 * 128, 128)
     args = lambda **kw: dict(dict(q=16, qs=qs, kc=32, vc=48, pages=10, bt=64, bts=4, sl=80, maxp=4, B=1,
-                                  Hq=4, Hkv=2, Lq=2, D=128, ps=16, S=2, scale=0.1, mask=None, wo=96, wl=112), **kw)
+                                  Hq=4, Hkv=2, Lq=2, D=128, dt=0, ps=16, S=2, scale=0.1, mask=None, wo=96,
+                                  wl=112), **kw)
 
     def dec(**kw):
         a = args(**kw)
         mk = None if a["mask"] is None else ctypes.byref(a["mask"])
         return lib.attn_decode_splitkv(a["q"], a["qs"], a["kc"], a["vc"], a["pages"], a["bt"], a["bts"],
                                        a["sl"], a["maxp"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"],
-                                       a["ps"], a["S"], a["scale"], mk, a["wo"], a["wl"], None)
+                                       a["dt"], a["ps"], a["S"], a["scale"], mk, a["wo"], a["wl"], None)
     assert dec(wo=None) == -1
     assert dec(S=0) == -8
     assert dec(bts=3) == -2
     assert dec(D=80) == -3
+    assert dec(dt=5) == -12
     assert dec(Hq=3) == -4
     md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=1, doc_stride=2)
     assert dec(mask=md) == -7
     assert dec(B=0) == 0
-    assert lib.attn_decode_combine(None, 16, 1, 1, 1, 1, 64, 32, qs, None, None) == -1
-    assert lib.attn_decode_combine(16, 16, 1, 1, 1, 0, 64, 32, qs, None, None) == -8
+    assert lib.attn_decode_combine(None, 16, 1, 1, 1, 1, 64, 0, 32, qs, None, None) == -1
+    assert lib.attn_decode_combine(16, 16, 1, 1, 1, 0, 64, 0, 32, qs, None, None) == -8
+    assert lib.attn_decode_combine(16, 16, 1, 1, 1, 1, 64, 3, 32, qs, None, None) == -12
     assert lib.attn_decode_num_splits(16, 8, 2048, 256) == 4   # two work groups per CU
     assert lib.attn_decode_num_splits(1, 1, 3, 256) == 3        # never more splits than pages
     assert lib.attn_decode_num_splits(1, 300, 10000, 256) == 5  # at most 2048 pages per split
@@ -133,18 +138,19 @@ def test_bwd_argument_errors(T):
 
     def bwd(**kw):
         a = dict(q=16, k=32, v=48, o=64, do=80, lse=96, dq=112, dk=128, dv=144, s=qs, ks=qs, B=1, Hq=1,
-                 Hkv=1, Nq=256, Nk=256, D=64, scale=0.125, mask=None, ws=160, wsb=ws)
+                 Hkv=1, Nq=256, Nk=256, D=64, dt=1, scale=0.125, mask=None, ws=160, wsb=ws)
         a.update(kw)
         mk = None if a["mask"] is None else ctypes.byref(a["mask"])
         s, ks = a["s"], a["ks"]
         return lib.attn_bwd(a["q"], s, a["k"], ks, a["v"], s, a["o"], s, a["do"], s, a["lse"], a["dq"], s,
                             a["dk"], s, a["dv"], s, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
-                            a["scale"], mk, a["ws"], a["wsb"], None)
+                            a["dt"], a["scale"], mk, a["ws"], a["wsb"], None)
     assert bwd(do=None) == -1
     assert bwd(lse=None) == -1
     assert bwd(dk=None) == -1
     assert bwd(ws=None) == -1
     assert bwd(D=32) == -3
+    assert bwd(dt=7) == -12
     assert bwd(Hq=2, Hkv=3) == -4
     assert bwd(s=_strides(64 * 256, 64 * 256, 68)) == -5
     assert bwd(ks=_strides(1 << 30, 1 << 30, 1 << 24)) == -5  # streamed row stride over 2^24

@@ -50,10 +50,10 @@ def _to_dev(x, layout):
     return x.to(DEV)
 
 
-def _empty_like_layout(B, H, N, D, layout):
+def _empty_like_layout(B, H, N, D, layout, dtype=torch.bfloat16):
     if layout == "bnhd":
-        return torch.full((B, N, H, D), float("nan"), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
-    return torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        return torch.full((B, N, H, D), float("nan"), dtype=dtype, device=DEV).transpose(1, 2)
+    return torch.full((B, H, N, D), float("nan"), dtype=dtype, device=DEV)
 
 
 def _fwd_bwd(q, k, v, do, scale, gm, layout="bhnd"):
@@ -61,12 +61,12 @@ def _fwd_bwd(q, k, v, do, scale, gm, layout="bhnd"):
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     qg, kg, vg, dog = (_to_dev(x, layout) for x in (q, k, v, do))
-    o = _empty_like_layout(B, Hq, Nq, D, layout)
+    o = _empty_like_layout(B, Hq, Nq, D, layout, q.dtype)
     lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device=DEV)
     T.attn_fwd(qg, kg, vg, o, lse, scale, gm)
-    dq = _empty_like_layout(B, Hq, Nq, D, layout)
-    dk = _empty_like_layout(B, Hkv, Nk, D, layout)
-    dv = _empty_like_layout(B, Hkv, Nk, D, layout)
+    dq = _empty_like_layout(B, Hq, Nq, D, layout, q.dtype)
+    dk = _empty_like_layout(B, Hkv, Nk, D, layout, q.dtype)
+    dv = _empty_like_layout(B, Hkv, Nk, D, layout, q.dtype)
     ws = torch.full((max(T.attn_bwd_workspace_bytes(B, Hq, Nq) // 4, 1),), float("nan"),
                     dtype=torch.float32, device=DEV)
     T.attn_bwd(qg, kg, vg, o, dog, lse, dq, dk, dv, ws, scale, gm)
@@ -95,20 +95,26 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd", "fp16"])
 def test_backward_matches_oracle(case, layout):
+    """bhnd / bnhd: bf16 in the two memory layouts; fp16: fp16 inputs in [B, H, N, D]."""
     name, B, Hq, Hkv, Nq, Nk, D, spec = case
     if layout == "bnhd" and name not in ("causal_d64_n300", "causal_d128_n257_gqa", "window_docs_d128"):
         pytest.skip("strided layout checked on a subset")
+    if layout == "fp16" and name not in ("causal_d64_n300", "causal_d128_n257_gqa", "window_docs_d128",
+                                         "causal_empty_rows_d128", "block_diffusion_d64_bs5"):
+        pytest.skip("fp16 checked on a subset")
     announce(f"bwd {name} {layout}")
+    dtype = torch.float16 if layout == "fp16" else torch.bfloat16
     g = W.generator(len(name) * 7 + Nq)
-    q = W.randn_bf16(g, (B, Hq, Nq, D))
-    k = W.randn_bf16(g, (B, Hkv, Nk, D))
-    v = W.randn_bf16(g, (B, Hkv, Nk, D))
-    do = W.randn_bf16(g, (B, Hq, Nq, D))
+    q = W.randn_half(g, (B, Hq, Nq, D), dtype)
+    k = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    v = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    do = W.randn_half(g, (B, Hq, Nq, D), dtype)
     scale = 1.0 / math.sqrt(D)
     gm, mod = _mask_pair(spec, B, Nq, Nk)
-    o, lse, dq, dk, dv = _fwd_bwd(q, k, v, do, scale, gm, layout)
+    o, lse, dq, dk, dv = _fwd_bwd(q, k, v, do, scale, gm, "bnhd" if layout == "bnhd" else "bhnd")
+    assert dq.dtype == dtype
     rq, rk, rv, (mq, mk, mv) = OBW.attention_bwd(f64(q), f64(k), f64(v), f64(do), scale, mod,
                                                  row_block=256, bound=True, o_used=f64(o))
     eq = assert_grad_close(f64(dq), rq, mq, f"{name} dQ")

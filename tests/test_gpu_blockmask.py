@@ -78,13 +78,14 @@ def test_builder_from_tile_map_bitwise():
         assert np.array_equal(bm.full_idx[0, h].cpu().numpy(), fi)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("D,Hq,Hkv,N", [(64, 4, 2, 1000), (128, 4, 1, 1300)])
-def test_fwd_blockmask_small_vs_oracle(D, Hq, Hkv, N):
-    announce(f"fwd_blockmask small D{D} N{N}")
+def test_fwd_blockmask_small_vs_oracle(D, Hq, Hkv, N, dtype):
+    announce(f"fwd_blockmask small D{D} N{N} {dtype}")
     g = W.generator(D + N)
-    q = W.randn_bf16(g, (1, Hq, N, D))
-    k = W.randn_bf16(g, (1, Hkv, N, D))
-    v = W.randn_bf16(g, (1, Hkv, N, D))
+    q = W.randn_half(g, (1, Hq, N, D), dtype)
+    k = W.randn_half(g, (1, Hkv, N, D), dtype)
+    v = W.randn_half(g, (1, Hkv, N, D), dtype)
     nt = (N + 127) // 128
     tm = W.blockmask_tile_map(g, nt, 0.3)
     tm[1, nt - 1] = W.TILE_FULL

@@ -43,7 +43,7 @@ def _run(q, k, v, scale, gm, layout="bhnd"):
         qg = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
         kg = k.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
         vg = v.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
-        o = torch.empty(B, Nq, Hq, D, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+        o = torch.empty(B, Nq, Hq, D, dtype=q.dtype, device=DEV).transpose(1, 2)
     else:
         qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
         o = torch.empty_like(qg)
@@ -98,6 +98,34 @@ def test_small_vs_oracle(case):
     o, lse = _run(q, k, v, scale, gm)
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
     assert_close(f64(o), f64(lse), ro, rl, name)
+
+
+FP16_CASES = ["none_d64", "causal_d64_n1000", "causal_d128_n1000", "causal_gqa_4_1",
+              "window_docs_d128", "block_diffusion_d128", "causal_bottom_right", "causal_d128_q600_k300"]
+
+
+@pytest.mark.parametrize("name", FP16_CASES)
+def test_fp16_vs_oracle(name):
+    """The same kernels instantiated for fp16 inputs (fp16 MFMAs, P rounded to fp16)."""
+    name_, B, Hq, Hkv, Nq, Nk, D, spec = next(c for c in SMALL if c[0] == name)
+    announce(f"fp16 {name}")
+    g = W.generator(zlib.crc32(name.encode()) % 9973 + 1)
+    q = W.randn_half(g, (B, Hq, Nq, D), torch.float16)
+    k = W.randn_half(g, (B, Hkv, Nk, D), torch.float16)
+    v = W.randn_half(g, (B, Hkv, Nk, D), torch.float16)
+    scale = 1.0 / math.sqrt(D)
+    gm, mod = _mask_pair(spec, B, Nq, Nk)
+    o, lse = _run(q, k, v, scale, gm, "bnhd" if name == "causal_gqa_4_1" else "bhnd")
+    assert o.dtype == torch.float16
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
+    assert_close(f64(o), f64(lse), ro, rl, f"fp16 {name}")
+
+
+def test_mixed_dtypes_rejected():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16, device=DEV)
+    k = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        T.attn_fwd(q, k, k, torch.empty_like(q), None, 0.125, None)
 
 
 @pytest.mark.parametrize("layout", ["bnhd"])

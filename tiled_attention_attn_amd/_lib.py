@@ -19,6 +19,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtiled_attn.so")
 
+DTYPE_BF16 = 0
+DTYPE_F16 = 1
+_DTYPES = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+
 MASK_CAUSAL = 1
 MASK_WINDOW = 2
 MASK_DOCUMENT = 4
@@ -65,17 +69,17 @@ def _load():
     MP = ctypes.POINTER(attn_mask_desc)
     BP = ctypes.POINTER(attn_blockmask)
     sig = {
-        "attn_fwd": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, F, MP, P]),
-        "attn_fwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, F, MP, BP, P]),
+        "attn_fwd": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, P]),
+        "attn_fwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, BP, P]),
         "attn_build_blockmask": (I, [MP, P, I, I, I, BP, P]),
         "attn_blockmask_bytes": (S, [I, I, I, I]),
-        "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, F, MP, P, P, P]),
-        "attn_decode_combine": (I, [P, P, I, I, I, I, I, P, STR, P, P]),
+        "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, I, F, MP, P, P, P]),
+        "attn_decode_combine": (I, [P, P, I, I, I, I, I, I, P, STR, P, P]),
         "attn_decode_ws_o_bytes": (S, [I, I, I, I, I]),
         "attn_decode_ws_lse_bytes": (S, [I, I, I, I]),
         "attn_decode_num_splits": (I, [I, I, I, I]),
         "attn_bwd": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
-                         I, I, I, I, I, I, F, MP, P, S, P]),
+                         I, I, I, I, I, I, I, F, MP, P, S, P]),
         "attn_bwd_workspace_bytes": (S, [I, I, I]),
         "attn_status_str": (ctypes.c_char_p, [I]),
         "attn_abi_version": (I, []),
@@ -118,12 +122,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _bf16(*ts):
+def _half(*ts):
+    """The library dtype code shared by all of ``ts`` (bf16 or fp16, D contiguous)."""
+    dt = ts[0].dtype
     for t in ts:
-        if t.dtype != torch.bfloat16:
-            raise TypeError("Q, K, V and O must be bfloat16")
+        if t.dtype != dt or dt not in _DTYPES:
+            raise TypeError("attention tensors must all be bfloat16 or all float16")
         if t.stride(-1) != 1:
             raise ValueError("the head dimension must be contiguous")
+    return _DTYPES[dt]
 
 
 @dataclass
@@ -174,14 +181,15 @@ def _mask_ptr(mask):
 
 
 def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None):
-    """O (and LSE) for q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] bf16 CUDA tensors (any B/H/N strides)."""
-    _bf16(q, k, v, o)
+    """O (and LSE) for q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] bf16 or fp16 CUDA tensors (any B/H/N
+    strides)."""
+    dt = _half(q, k, v, o)
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     st = _lib.attn_fwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-                       _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, scale, mp,
+                       _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale, mp,
                        _stream(stream))
     _check("attn_fwd", st)
     return o, lse
@@ -224,14 +232,14 @@ def attn_build_blockmask(bm: BlockMask, B, Nq, Nk, mask=None, tile_map=None, str
 
 
 def attn_fwd_blockmask(q, k, v, o, bm: BlockMask, lse=None, scale=None, mask=None, stream=None):
-    _bf16(q, k, v, o)
+    dt = _half(q, k, v, o)
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     s = bm.struct()
     st = _lib.attn_fwd_blockmask(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-                                 _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, scale,
+                                 _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale,
                                  mp, ctypes.byref(s), _stream(stream))
     _check("attn_fwd_blockmask", st)
     return o, lse
@@ -256,9 +264,9 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, n
     """Split-KV partials: q [B,Hq,Lq,D]; caches [pages, page_size, Hkv, D] (contiguous);
     block_table int32 [B, >=max_pages]; seq_lens int32 [B]; ws_o float [B,Hq,Lq,S,D];
     ws_lse float [B,Hq,Lq,S]."""
-    _bf16(q)
-    if k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
-        raise TypeError("KV caches must be bfloat16")
+    dt = _half(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("KV caches must have the dtype of q")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("KV caches must be contiguous [pages, page_size, Hkv, D]")
     if k_cache.shape != v_cache.shape:
@@ -280,20 +288,20 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, n
     keep, mp = _mask_ptr(mask)
     st = _lib.attn_decode_splitkv(_ptr(q), _strides(q), _ptr(k_cache), _ptr(v_cache), n_pages,
                                   _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
-                                  int(max_pages), B, Hq, Hkv, Lq, D, page_size, int(num_splits),
+                                  int(max_pages), B, Hq, Hkv, Lq, D, dt, page_size, int(num_splits),
                                   scale, mp, _ptr(ws_o), _ptr(ws_lse), _stream(stream))
     _check("attn_decode_splitkv", st)
     return ws_o, ws_lse
 
 
 def attn_decode_combine(ws_o, ws_lse, o, lse=None, stream=None):
-    """O [B,Hq,Lq,D] bf16 (and LSE [B,Hq,Lq]) from ws_o [B,Hq,Lq,S,D], ws_lse [B,Hq,Lq,S]."""
-    _bf16(o)
+    """O [B,Hq,Lq,D] bf16 / fp16 (and LSE [B,Hq,Lq]) from ws_o [B,Hq,Lq,S,D], ws_lse [B,Hq,Lq,S]."""
+    dt = _half(o)
     B, Hq, Lq, S, D = ws_o.shape
     if ws_o.dtype != torch.float32 or not ws_o.is_contiguous() or not ws_lse.is_contiguous():
         raise TypeError("workspaces must be contiguous float32")
-    st = _lib.attn_decode_combine(_ptr(ws_o), _ptr(ws_lse), B, Hq, Lq, S, D, _ptr(o), _strides(o),
-                                  _ptr(lse), _stream(stream))
+    st = _lib.attn_decode_combine(_ptr(ws_o), _ptr(ws_lse), B, Hq, Lq, S, D, dt, _ptr(o),
+                                  _strides(o), _ptr(lse), _stream(stream))
     _check("attn_decode_combine", st)
     return o, lse
 
@@ -303,10 +311,10 @@ def attn_bwd_workspace_bytes(B, Hq, Nq):
 
 
 def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=None, stream=None):
-    """dQ, dK, dV (bf16, written into dq / dk / dv) for q/o/d_o [B,Hq,Nq,D], k/v [B,Hkv,Nk,D]
+    """dQ, dK, dV (written into dq / dk / dv) for q/o/d_o [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] (bf16 or fp16)
     and the forward pass's lse float [B,Hq,Nq]; ``workspace`` is a float32 CUDA tensor of at
     least attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here if None)."""
-    _bf16(q, k, v, o, d_o, dq, dk, dv)
+    dt = _half(q, k, v, o, d_o, dq, dk, dv)
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     if lse.dtype != torch.float32 or not lse.is_contiguous():
@@ -321,7 +329,7 @@ def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=
     st = _lib.attn_bwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                        _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse),
                        _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
-                       B, Hq, Hkv, Nq, Nk, D, scale, mp, _ptr(workspace), workspace.numel() * 4,
+                       B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, _ptr(workspace), workspace.numel() * 4,
                        _stream(stream))
     _check("attn_bwd", st)
     return dq, dk, dv

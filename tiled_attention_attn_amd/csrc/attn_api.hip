@@ -8,13 +8,13 @@
 #include "params.h"
 
 namespace tattn {
-int launch_fwd(const FwdParams& p, int D, bool blockmask, hipStream_t stream);
+int launch_fwd(const FwdParams& p, int D, bool blockmask, int dtype, hipStream_t stream);
 int launch_blockmask(const BmBuildParams& p, hipStream_t stream);
-int launch_decode(const DecParams& p, int D, hipStream_t stream);
+int launch_decode(const DecParams& p, int D, int dtype, hipStream_t stream);
 int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
-                   bf16* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
+                   int dtype, void* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
                    hipStream_t stream);
-int launch_bwd(const BwdParams& p, int D, hipStream_t stream);
+int launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t stream);
 }  // namespace tattn
 
 using namespace tattn;
@@ -35,6 +35,10 @@ int check_strides(const int64_t s[3]) {
 
 int check_scale(float scale) {
   return (std::isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
+}
+
+int check_dtype(int dtype) {
+  return (dtype == ATTN_DTYPE_BF16 || dtype == ATTN_DTYPE_F16) ? ATTN_OK : ATTN_ERR_DTYPE;
 }
 
 // Converts the public mask descriptor; `allow_doc` is false for decode.
@@ -63,7 +67,7 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
 
 int check_common(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
                  const void* v, const int64_t* vs, const void* o, const int64_t* os, int B,
-                 int Hq, int Hkv, int Nq, int Nk, int D, float scale) {
+                 int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale) {
   // K and V may be NULL when there are no keys (an empty tensor has no storage).
   if (!q || !o || (Nk > 0 && (!k || !v))) return ATTN_ERR_NULL;
   int st;
@@ -73,6 +77,7 @@ int check_common(const void* q, const int64_t* qs, const void* k, const int64_t*
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
   if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if ((st = check_dtype(dtype))) return st;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!aligned16(q) || !aligned16(o) || (Nk > 0 && (!aligned16(k) || !aligned16(v))))
     return ATTN_ERR_ALIGN;
@@ -85,10 +90,10 @@ int check_common(const void* q, const int64_t* qs, const void* k, const int64_t*
 void fill_fwd(FwdParams& p, const void* q, const int64_t* qs, const void* k, const int64_t* ks,
               const void* v, const int64_t* vs, void* o, const int64_t* os, float* lse, int B,
               int Hq, int Hkv, int Nq, int Nk, float scale) {
-  p.q = static_cast<const bf16*>(q);
-  p.k = static_cast<const bf16*>(k);
-  p.v = static_cast<const bf16*>(v);
-  p.o = static_cast<bf16*>(o);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
   p.lse = lse;
   p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sn = qs[2];
   p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sn = ks[2];
@@ -118,7 +123,7 @@ void set_slots(FwdParams& p, bool paired) {
 
 extern "C" {
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -134,16 +139,17 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_LAUNCH: return "the HIP runtime reported a launch error";
     case ATTN_ERR_BLOCKMASK: return "BlockMask descriptor inconsistent with the shapes";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_DTYPE: return "dtype must be ATTN_DTYPE_BF16 or ATTN_DTYPE_F16";
     default: return "unknown status";
   }
 }
 
 int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
              const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3],
-             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int D, float scale,
+             float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
              const attn_mask_desc* mask, hipStream_t stream) {
   int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
-                        D, scale);
+                        D, dtype, scale);
   if (st) return st;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
@@ -151,7 +157,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
   set_slots(p, causal_like(p.mask));
-  return launch_fwd(p, D, false, stream);
+  return launch_fwd(p, D, false, dtype, stream);
 }
 
 size_t attn_blockmask_bytes(int Bm, int Hm, int nQt, int nKt) {
@@ -188,10 +194,10 @@ int attn_build_blockmask(const attn_mask_desc* mask, const uint8_t* tile_map, in
 int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
                        const int64_t k_stride[3], const void* v, const int64_t v_stride[3],
                        void* o, const int64_t o_stride[3], float* lse, int B, int Hq, int Hkv,
-                       int Nq, int Nk, int D, float scale, const attn_mask_desc* mask,
+                       int Nq, int Nk, int D, int dtype, float scale, const attn_mask_desc* mask,
                        const attn_blockmask* bm, hipStream_t stream) {
   int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
-                        D, scale);
+                        D, dtype, scale);
   if (st) return st;
   if (bm == nullptr) return ATTN_ERR_NULL;
   if (!bm->part_num || !bm->part_idx || !bm->full_num || !bm->full_idx) return ATTN_ERR_NULL;
@@ -205,7 +211,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   p.full_num = bm->full_num; p.full_idx = bm->full_idx;
   p.bm_B = bm->Bm; p.bm_H = bm->Hm;
   set_slots(p, true);
-  return launch_fwd(p, D, true, stream);
+  return launch_fwd(p, D, true, dtype, stream);
 }
 
 size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits) {
@@ -237,7 +243,7 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
 int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_cache,
                         const void* v_cache, int64_t num_pages, const int32_t* block_table,
                         int64_t bt_stride, const int32_t* seq_lens, int max_pages, int B, int Hq,
-                        int Hkv, int Lq, int D, int page_size, int num_splits, float scale,
+                        int Hkv, int Lq, int D, int dtype, int page_size, int num_splits, float scale,
                         const attn_mask_desc* mask, float* ws_o, float* ws_lse,
                         hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !ws_o || !ws_lse)
@@ -250,6 +256,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   if ((int64_t)max_pages * page_size > kMaxLen) return ATTN_ERR_SHAPE;
   if (bt_stride < max_pages) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if ((st = check_dtype(dtype))) return st;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws_o))
     return ATTN_ERR_ALIGN;
@@ -262,10 +269,10 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
-  p.q = static_cast<const bf16*>(q);
+  p.q = q;
   p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
-  p.kc = static_cast<const bf16*>(k_cache);
-  p.vc = static_cast<const bf16*>(v_cache);
+  p.kc = k_cache;
+  p.vc = v_cache;
   p.bt = block_table;
   p.bt_stride = bt_stride;
   p.seq_lens = seq_lens;
@@ -279,11 +286,11 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   p.c2 = scale * 1.4426950408889634f;
   p.ws_o = ws_o;
   p.ws_lse = ws_lse;
-  return launch_decode(p, D, stream);
+  return launch_decode(p, D, dtype, stream);
 }
 
 int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S,
-                        int D, void* o, const int64_t o_stride[3], float* lse,
+                        int D, int dtype, void* o, const int64_t o_stride[3], float* lse,
                         hipStream_t stream) {
   if (!ws_o || !ws_lse || !o) return ATTN_ERR_NULL;
   int st = check_strides(o_stride);
@@ -291,11 +298,12 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, i
   if (B < 0 || Hq < 0 || Lq < 0) return ATTN_ERR_SHAPE;
   if ((long)B * Hq * Lq > 0x7fffffffL) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if ((st = check_dtype(dtype))) return st;
   if (S < 1 || S > 65536) return ATTN_ERR_WORKSPACE;
   if (!aligned16(o) || !aligned16(ws_o)) return ATTN_ERR_ALIGN;
   if (B == 0 || Hq == 0 || Lq == 0) return ATTN_OK;
-  return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, static_cast<bf16*>(o), o_stride[0],
-                        o_stride[1], o_stride[2], lse, stream);
+  return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, dtype, o, o_stride[0], o_stride[1],
+                        o_stride[2], lse, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
@@ -309,8 +317,8 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
              const void* d_o, const int64_t do_stride[3], const float* lse, void* dq,
              const int64_t dq_stride[3], void* dk, const int64_t dk_stride[3], void* dv,
              const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
-             float scale, const attn_mask_desc* mask, float* workspace, size_t workspace_bytes,
-             hipStream_t stream) {
+             int dtype, float scale, const attn_mask_desc* mask, float* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
   // Tensors without rows may be NULL (an empty tensor has no storage).
   if (Nq > 0 && (!q || !o || !d_o || !dq || !lse)) return ATTN_ERR_NULL;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
@@ -323,6 +331,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
   if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if ((st = check_dtype(dtype))) return st;
   if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
   const void* ptrs[9] = {q, k, v, o, d_o, dq, dk, dv, workspace};
   for (const void* x : ptrs)
@@ -337,15 +346,15 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
-  p.q = static_cast<const bf16*>(q);
-  p.k = static_cast<const bf16*>(k);
-  p.v = static_cast<const bf16*>(v);
-  p.o = static_cast<const bf16*>(o);
-  p.dout = static_cast<const bf16*>(d_o);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = d_o;
   p.lse = lse;
-  p.dq = static_cast<bf16*>(dq);
-  p.dk = static_cast<bf16*>(dk);
-  p.dv = static_cast<bf16*>(dv);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
   p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
   p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
   p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
@@ -371,7 +380,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   p.q_paired = pair && p.n_qt > 1;
   p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
   p.q_xcd_remap = ((long)B * Hq * p.q_slots) % 8 == 0;
-  return launch_bwd(p, D, stream);
+  return launch_bwd(p, D, dtype, stream);
 }
 
 }  // extern "C"

@@ -26,9 +26,9 @@
 //    written once.
 //
 // gfx950 mapping (the operand layouts of the forward kernel):
-//  * kv kernel: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 with
+//  * kv kernel: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 (_f16) with
 //    queries as M and the wave's keys as N, so each lane owns one key column.
-//    Those accumulators, converted to bf16, are directly the B operands of
+//    Those accumulators, converted to bf16 / fp16, are directly the B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS; the A operands dO^T and Q^T come from
 //    LDS with ds_read_b64_tr_b16, with the 16 queries of each MFMA permuted
 //    the same way as the accumulator rows.
@@ -50,7 +50,7 @@ constexpr int kBwdThreads = 256;
 // ---- Delta and L2 per query row ----------------------------------------------
 // Eight lanes per row, 16-byte loads; rows of a (batch, head) padded to
 // nq_pad get Delta = 0 and L2 = +inf.
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(kBwdThreads) bwd_pre_kernel(const BwdParams p) {
   const int64_t row = ((int64_t)blockIdx.x * kBwdThreads + threadIdx.x) >> 3;
   const int j = threadIdx.x & 7;
@@ -60,12 +60,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_pre_kernel(const BwdParams p)
   const int b = bh / p.Hq, h = bh % p.Hq;
   float acc = 0.f;
   if (qi < p.Nq) {
-    const bf16* orow = p.o + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
-    const bf16* drow = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)qi * p.do_sn;
+    const T* orow = static_cast<const T*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qi * p.o_sn;
+    const T* drow = static_cast<const T*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)qi * p.do_sn;
 #pragma unroll
     for (int c = j; c < D / 8; c += 8) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + 8 * c);
-      const bf16x8 d = *reinterpret_cast<const bf16x8*>(drow + 8 * c);
+      const vec8<T> a = *reinterpret_cast<const vec8<T>*>(orow + 8 * c);
+      const vec8<T> d = *reinterpret_cast<const vec8<T>*>(drow + 8 * c);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)a[i], (float)d[i], acc);
     }
@@ -109,7 +109,7 @@ __device__ __forceinline__ void key_rows(const MaskParams& m, int b, int key, in
 // 8 KB either way; a stage adds 1 KB for L2 and Delta).
 template <int D> struct BwdQRows { static constexpr int value = D == 64 ? 64 : 32; };
 
-template <int D>
+template <int D, typename T>
 __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem, int kt, int b,
                                         int kvh) {
   constexpr int QB = BwdQRows<D>::value;
@@ -132,15 +132,15 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 
   // K and V of the lane's key: B operands of S = Q K^T and dP = dO V^T
   // (k = head dim, n = key).
-  bf16x8 kf[NC], vf[NC];
+  vec8<T> kf[NC], vf[NC];
   {
     const int r = key_ok ? key : p.Nk - 1;
-    const bf16* ks = p.k + b * p.k_sb + kvh * p.k_sh + (int64_t)r * p.k_sn + 8 * half;
-    const bf16* vs = p.v + b * p.v_sb + kvh * p.v_sh + (int64_t)r * p.v_sn + 8 * half;
+    const T* ks = static_cast<const T*>(p.k) + b * p.k_sb + kvh * p.k_sh + (int64_t)r * p.k_sn + 8 * half;
+    const T* vs = static_cast<const T*>(p.v) + b * p.v_sb + kvh * p.v_sh + (int64_t)r * p.v_sn + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kf[c] = *reinterpret_cast<const bf16x8*>(ks + 16 * c);
-      vf[c] = *reinterpret_cast<const bf16x8*>(vs + 16 * c);
+      kf[c] = *reinterpret_cast<const vec8<T>*>(ks + 16 * c);
+      vf[c] = *reinterpret_cast<const vec8<T>*>(vs + 16 * c);
     }
     wait_vmem();
   }
@@ -215,16 +215,16 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 
   // Steps run head-major: (g, qi) for g < G, qi < n_qs; a cursor per
   // direction (copies issued, steps computed) advances without divisions.
-  const bf16* q_head = p.q + b * p.q_sb + (int64_t)kvh * p.G * p.q_sh;
-  const bf16* do_head = p.dout + b * p.do_sb + (int64_t)kvh * p.G * p.do_sh;
+  const T* q_head = static_cast<const T*>(p.q) + b * p.q_sb + (int64_t)kvh * p.G * p.q_sh;
+  const T* do_head = static_cast<const T*>(p.dout) + b * p.do_sb + (int64_t)kvh * p.G * p.do_sh;
   const float* ws_head = p.ws_l2 + (int64_t)(b * p.Hq + kvh * p.G) * p.nq_pad;
   const int64_t ws_delta_off = p.ws_delta - p.ws_l2;
   int ld_g = 0, ld_qi = 0;
   auto load_next = [&](int stage) {
     const int q0 = qs0 + ld_qi * QB;
     const uint32_t lb = lds_addr(smem) + stage * STAGE_BYTES;
-    const bf16* qbase = q_head + ld_g * p.q_sh + (int64_t)q0 * p.q_sn;
-    const bf16* dbase = do_head + ld_g * p.do_sh + (int64_t)q0 * p.do_sn;
+    const T* qbase = q_head + ld_g * p.q_sh + (int64_t)q0 * p.q_sn;
+    const T* dbase = do_head + ld_g * p.do_sh + (int64_t)q0 * p.do_sn;
     if (q0 + QB <= p.Nq) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -278,8 +278,8 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       sacc[blk] = dpacc[blk] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        sacc[blk] = mfma32(lds_read_b128(tQ, a_addr[c] + roff), kf[c], sacc[blk]);
-        dpacc[blk] = mfma32(lds_read_b128(tD, a_addr[c] + roff), vf[c], dpacc[blk]);
+        sacc[blk] = mfma32(lds_read_b128<T>(tQ, a_addr[c] + roff), kf[c], sacc[blk]);
+        dpacc[blk] = mfma32(lds_read_b128<T>(tD, a_addr[c] + roff), vf[c], dpacc[blk]);
       }
     }
     // Keep the operand reads about four MFMAs ahead of their use.
@@ -319,12 +319,12 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
         pr[r] = fast_exp2(__builtin_fmaf(sacc[blk][r], p.c2, -l2[r >> 2][r & 3]));
         ds[r] = pr[r] * (dpacc[blk][r] - dl[r >> 2][r & 3]);
       }
-      bf16x8 pp[2], pd[2];
+      vec8<T> pp[2], pd[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        pp[c] = pack8(pr[8 * c], pr[8 * c + 1], pr[8 * c + 2], pr[8 * c + 3], pr[8 * c + 4],
+        pp[c] = pack8<T>(pr[8 * c], pr[8 * c + 1], pr[8 * c + 2], pr[8 * c + 3], pr[8 * c + 4],
                       pr[8 * c + 5], pr[8 * c + 6], pr[8 * c + 7]);
-        pd[c] = pack8(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3], ds[8 * c + 4],
+        pd[c] = pack8<T>(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3], ds[8 * c + 4],
                       ds[8 * c + 5], ds[8 * c + 6], ds[8 * c + 7]);
       }
       // ---- dV^T += dO^T P and dK^T += Q^T dS over these 32 rows ----
@@ -334,10 +334,10 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
         for (int db = 0; db < NDB; ++db) {
           const i16x4 a0 = lds_read_tr16(tD, t_addr[c][db][0] + roff);
           const i16x4 a1 = lds_read_tr16(tD, t_addr[c][db][1] + roff);
-          dv[db] = mfma32(join_tr(a0, a1), pp[c], dv[db]);
+          dv[db] = mfma32(join_tr<T>(a0, a1), pp[c], dv[db]);
           const i16x4 b0 = lds_read_tr16(tQ, t_addr[c][db][0] + roff);
           const i16x4 b1 = lds_read_tr16(tQ, t_addr[c][db][1] + roff);
-          dk[db] = mfma32(join_tr(b0, b1), pd[c], dk[db]);
+          dk[db] = mfma32(join_tr<T>(b0, b1), pd[c], dk[db]);
         }
     }
   };
@@ -350,18 +350,17 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 
   // ---- epilogue: lane owns key `key`, d = 32 db + 8 (r/4) + 4 half + r%4 ----
   if (key_ok) {
-    bf16* dkrow = p.dk + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_sn;
-    bf16* dvrow = p.dv + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_sn;
+    T* dkrow = static_cast<T*>(p.dk) + b * p.dk_sb + kvh * p.dk_sh + (int64_t)key * p.dk_sn;
+    T* dvrow = static_cast<T*>(p.dv) + b * p.dv_sb + kvh * p.dv_sh + (int64_t)key * p.dv_sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x2 a = pack2(dk[db][4 * r4] * p.scale, dk[db][4 * r4 + 1] * p.scale);
-        const bf16x2 c = pack2(dk[db][4 * r4 + 2] * p.scale, dk[db][4 * r4 + 3] * p.scale);
-        *reinterpret_cast<bf16x4*>(dkrow + 32 * db + 8 * r4 + 4 * half) = bf16x4{a[0], a[1], c[0], c[1]};
-        const bf16x2 e = pack2(dv[db][4 * r4], dv[db][4 * r4 + 1]);
-        const bf16x2 f = pack2(dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]);
-        *reinterpret_cast<bf16x4*>(dvrow + 32 * db + 8 * r4 + 4 * half) = bf16x4{e[0], e[1], f[0], f[1]};
+        *reinterpret_cast<vec4<T>*>(dkrow + 32 * db + 8 * r4 + 4 * half) =
+            pack4<T>(dk[db][4 * r4] * p.scale, dk[db][4 * r4 + 1] * p.scale,
+                     dk[db][4 * r4 + 2] * p.scale, dk[db][4 * r4 + 3] * p.scale);
+        *reinterpret_cast<vec4<T>*>(dvrow + 32 * db + 8 * r4 + 4 * half) =
+            pack4<T>(dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]);
       }
   }
 }
@@ -371,7 +370,7 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 // 512-entry register file of one SIMD lane.
 template <int D> struct BwdKvOcc { static constexpr int value = D == 64 ? 2 : 1; };
 
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(kBwdThreads)
 __attribute__((amdgpu_waves_per_eu(BwdKvOcc<D>::value, BwdKvOcc<D>::value)))
 bwd_kv_kernel(const BwdParams p) {
@@ -387,12 +386,12 @@ bwd_kv_kernel(const BwdParams p) {
   const int slot = unit % p.kv_slots;
   const int r = unit / p.kv_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
-  kv_tile<D>(p, smem, slot, b, kvh);
+  kv_tile<D, T>(p, smem, slot, b, kvh);
   if (p.kv_paired) {
     const int kt2 = p.n_kt - 1 - slot;
     if (kt2 != slot) {
       __syncthreads();
-      kv_tile<D>(p, smem, kt2, b, kvh);
+      kv_tile<D, T>(p, smem, kt2, b, kvh);
     }
   }
 }
@@ -401,7 +400,7 @@ bwd_kv_kernel(const BwdParams p) {
 // Keys per step as in the forward kernel: 128 at D=64, 64 at D=128.
 template <int D> struct BwdKBlk { static constexpr int value = D == 64 ? 128 : 64; };
 
-template <int D>
+template <int D, typename T>
 __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem, int qt, int b,
                                        int h, int kvh) {
   constexpr int kKBlk = BwdKBlk<D>::value;
@@ -424,15 +423,15 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
   const int rr = row_ok ? qrow : p.Nq - 1;
 
   // Q^T and dO^T: B operands of S^T = K Q^T and dP^T = V dO^T.
-  bf16x8 qf[NC], df[NC];
+  vec8<T> qf[NC], df[NC];
   float l2, dl;
   {
-    const bf16* qs = p.q + b * p.q_sb + h * p.q_sh + (int64_t)rr * p.q_sn + 8 * half;
-    const bf16* ds = p.dout + b * p.do_sb + h * p.do_sh + (int64_t)rr * p.do_sn + 8 * half;
+    const T* qs = static_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)rr * p.q_sn + 8 * half;
+    const T* ds = static_cast<const T*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)rr * p.do_sn + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(qs + 16 * c);
-      df[c] = *reinterpret_cast<const bf16x8*>(ds + 16 * c);
+      qf[c] = *reinterpret_cast<const vec8<T>*>(qs + 16 * c);
+      df[c] = *reinterpret_cast<const vec8<T>*>(ds + 16 * c);
     }
     const int64_t w = (int64_t)(b * p.Hq + h) * p.nq_pad + rr;
     l2 = p.ws_l2[w];
@@ -485,13 +484,13 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
         }
   }
 
-  const bf16* Kbh = p.k + b * p.k_sb + kvh * p.k_sh;
-  const bf16* Vbh = p.v + b * p.v_sb + kvh * p.v_sh;
+  const T* Kbh = static_cast<const T*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const T* Vbh = static_cast<const T*>(p.v) + b * p.v_sb + kvh * p.v_sh;
   auto load_step = [&](int s, int stage) {
     const int kb = kb_begin + s * kKBlk;
     const uint32_t lk = lds_addr(smem) + stage * STAGE_BYTES;
-    const bf16* kbase = Kbh + (int64_t)kb * p.k_sn;
-    const bf16* vbase = Vbh + (int64_t)kb * p.v_sn;
+    const T* kbase = Kbh + (int64_t)kb * p.k_sn;
+    const T* vbase = Vbh + (int64_t)kb * p.v_sn;
     if (kb + kKBlk <= p.Nk) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -531,10 +530,10 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sacc = mfma32(lds_read_b128(tK, k_addr[c] + kbk * 32 * ROW_BYTES), qf[c], sacc);
+        sacc = mfma32(lds_read_b128<T>(tK, k_addr[c] + kbk * 32 * ROW_BYTES), qf[c], sacc);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        dpacc = mfma32(lds_read_b128(tV, k_addr[c] + kbk * 32 * ROW_BYTES), df[c], dpacc);
+        dpacc = mfma32(lds_read_b128<T>(tV, k_addr[c] + kbk * 32 * ROW_BYTES), df[c], dpacc);
       // element r holds key kb + 32 kbk + 8 (r/4) + 4 half + r%4
       if (masked) {
 #pragma unroll
@@ -550,7 +549,7 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
       // ---- dQ^T += K^T dS^T over these 32 keys (two 16-key chunks) ----
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pd = pack8(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3],
+        const vec8<T> pd = pack8<T>(ds[8 * c], ds[8 * c + 1], ds[8 * c + 2], ds[8 * c + 3],
                                 ds[8 * c + 4], ds[8 * c + 5], ds[8 * c + 6], ds[8 * c + 7]);
         const int kc = 2 * kbk + c;
         const uint32_t kc_off = (kc / KC_PERIOD) * (16 * KC_PERIOD) * ROW_BYTES;
@@ -558,7 +557,7 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
         for (int db = 0; db < NDB; ++db) {
           const i16x4 a0 = lds_read_tr16(tK, t_addr[kc % KC_PERIOD][db][0] + kc_off);
           const i16x4 a1 = lds_read_tr16(tK, t_addr[kc % KC_PERIOD][db][1] + kc_off);
-          dq[db] = mfma32(join_tr(a0, a1), pd, dq[db]);
+          dq[db] = mfma32(join_tr<T>(a0, a1), pd, dq[db]);
         }
       }
     }
@@ -571,19 +570,19 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
   }
 
   if (row_ok) {
-    bf16* drow = p.dq + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_sn;
+    T* drow = static_cast<T*>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qrow * p.dq_sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x2 a = pack2(dq[db][4 * r4] * p.scale, dq[db][4 * r4 + 1] * p.scale);
-        const bf16x2 c = pack2(dq[db][4 * r4 + 2] * p.scale, dq[db][4 * r4 + 3] * p.scale);
-        *reinterpret_cast<bf16x4*>(drow + 32 * db + 8 * r4 + 4 * half) = bf16x4{a[0], a[1], c[0], c[1]};
+        *reinterpret_cast<vec4<T>*>(drow + 32 * db + 8 * r4 + 4 * half) =
+            pack4<T>(dq[db][4 * r4] * p.scale, dq[db][4 * r4 + 1] * p.scale,
+                     dq[db][4 * r4 + 2] * p.scale, dq[db][4 * r4 + 3] * p.scale);
       }
   }
 }
 
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2];
@@ -600,30 +599,36 @@ bwd_q_kernel(const BwdParams p) {
   r /= p.q_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  q_tile<D>(p, smem, slot, b, h, kvh);
+  q_tile<D, T>(p, smem, slot, b, h, kvh);
   if (p.q_paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      q_tile<D>(p, smem, qt2, b, h, kvh);
+      q_tile<D, T>(p, smem, qt2, b, h, kvh);
     }
   }
 }
 
-int launch_bwd(const BwdParams& p, int D, hipStream_t stream) {
+template <int D, typename T>
+void launch_bwd_t(const BwdParams& p, dim3 gpre, dim3 gkv, dim3 gq, dim3 block, hipStream_t stream) {
+  if (gpre.x) hipLaunchKernelGGL((bwd_pre_kernel<D, T>), gpre, block, 0, stream, p);
+  if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T>), gkv, block, 0, stream, p);
+  if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T>), gq, block, 0, stream, p);
+}
+
+int launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.nq_pad;
   const dim3 block(kBwdThreads);
   const dim3 gpre((unsigned)((rows * 8 + kBwdThreads - 1) / kBwdThreads));
   const dim3 gkv((unsigned)((int64_t)p.B * p.Hkv * p.kv_slots));
   const dim3 gq((unsigned)((int64_t)p.B * p.Hq * p.q_slots));
+  const bool f16in = dtype == ATTN_DTYPE_F16;
   if (D == 64) {
-    if (gpre.x) hipLaunchKernelGGL(bwd_pre_kernel<64>, gpre, block, 0, stream, p);
-    if (gkv.x) hipLaunchKernelGGL(bwd_kv_kernel<64>, gkv, block, 0, stream, p);
-    if (gq.x) hipLaunchKernelGGL(bwd_q_kernel<64>, gq, block, 0, stream, p);
+    if (f16in) launch_bwd_t<64, f16>(p, gpre, gkv, gq, block, stream);
+    else launch_bwd_t<64, bf16>(p, gpre, gkv, gq, block, stream);
   } else {
-    if (gpre.x) hipLaunchKernelGGL(bwd_pre_kernel<128>, gpre, block, 0, stream, p);
-    if (gkv.x) hipLaunchKernelGGL(bwd_kv_kernel<128>, gkv, block, 0, stream, p);
-    if (gq.x) hipLaunchKernelGGL(bwd_q_kernel<128>, gq, block, 0, stream, p);
+    if (f16in) launch_bwd_t<128, f16>(p, gpre, gkv, gq, block, stream);
+    else launch_bwd_t<128, bf16>(p, gpre, gkv, gq, block, stream);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

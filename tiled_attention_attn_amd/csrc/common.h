@@ -1,6 +1,8 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, MFMA
-// and LDS-transpose wrappers, cross-half exchanges, bf16 packing and the
-// per-row mask interval.
+// and LDS-transpose wrappers, cross-half exchanges, bf16 / fp16 packing and
+// the per-row mask interval.  Q, K, V and O are 16-bit floats of one type T,
+// bf16 or fp16; both have the same layouts, so every kernel is a template on
+// T and only the MFMA opcode and the conversions differ.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,12 +16,24 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define TATTN_LDS __attribute__((address_space(3)))
+
+// Vectors of the element type T (bf16 or f16).
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 x8; typedef bf16x4 x4; typedef bf16x2 x2; };
+template <> struct Vec<f16> { typedef f16x8 x8; typedef f16x4 x4; typedef f16x2 x2; };
+template <typename T> using vec8 = typename Vec<T>::x8;
+template <typename T> using vec4 = typename Vec<T>::x4;
+template <typename T> using vec2 = typename Vec<T>::x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -29,17 +43,25 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // 32x32x16 bf16: lane l holds A[m=l%32][k=8(l/32)+i], B[k=8(l/32)+i][n=l%32],
 // C[m=8(r/4)+4(l/32)+r%4][n=l%32].  16x16x32 bf16: A[m=l%16][k=8(l/16)+i],
 // B[k=8(l/16)+i][n=l%16], C[m=4(l/16)+r][n=l%16].  (Checked on gfx950 with an
-// in-bounds probe of every lane and slot.)
+// in-bounds probe of every lane and slot.)  The fp16 opcodes of the same
+// shapes use the same register layouts.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // ---- LDS access --------------------------------------------------------------
-__device__ __forceinline__ bf16x8 lds_read_b128(const TATTN_LDS char* base, uint32_t byte_off) {
-  return *reinterpret_cast<const TATTN_LDS bf16x8*>(base + byte_off);
+template <typename T>
+__device__ __forceinline__ vec8<T> lds_read_b128(const TATTN_LDS char* base, uint32_t byte_off) {
+  return *reinterpret_cast<const TATTN_LDS vec8<T>*>(base + byte_off);
 }
 
 // ds_read_b64_tr_b16.  Within each 16-lane group, lane j reads 4 halfwords
@@ -52,10 +74,11 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const TATTN_LDS char* base, uint3
       reinterpret_cast<TATTN_LDS i16x4*>(const_cast<TATTN_LDS char*>(base) + byte_off));
 }
 
-__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+template <typename T>
+__device__ __forceinline__ vec8<T> join_tr(i16x4 lo, i16x4 hi) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(vec8<T>, v);
 }
 
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's
@@ -130,20 +153,28 @@ __device__ __forceinline__ float other_half(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// fp32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+// fp32 -> T, round to nearest even (v_cvt_pk_bf16_f32 for bf16).
+template <typename T>
+__device__ __forceinline__ vec2<T> pack2(float a, float b) {
   f32x2 v = {a, b};
-  return __builtin_convertvector(v, bf16x2);
+  return __builtin_convertvector(v, vec2<T>);
 }
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
-                                        float a5, float a6, float a7) {
-  bf16x2 p0 = pack2(a0, a1), p1 = pack2(a2, a3), p2 = pack2(a4, a5), p3 = pack2(a6, a7);
-  bf16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+template <typename T>
+__device__ __forceinline__ vec8<T> pack8(float a0, float a1, float a2, float a3, float a4,
+                                         float a5, float a6, float a7) {
+  vec2<T> p0 = pack2<T>(a0, a1), p1 = pack2<T>(a2, a3), p2 = pack2<T>(a4, a5), p3 = pack2<T>(a6, a7);
+  vec8<T> r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ vec4<T> pack4(float a0, float a1, float a2, float a3) {
+  vec2<T> p0 = pack2<T>(a0, a1), p1 = pack2<T>(a2, a3);
+  vec4<T> r = {p0[0], p0[1], p1[0], p1[1]};
   return r;
 }
 
 // ---- K/V tiles in LDS --------------------------------------------------------
-// A tile is `rows` key rows of D bf16 (2D bytes each).  The 16-byte chunks of
+// A tile is `rows` key rows of D 16-bit elements (2D bytes each).  The 16-byte chunks of
 // row r are XOR-swizzled by Swz<D>::f(r), which keeps both the ds_read_b128
 // K-operand reads (one chunk of 32 consecutive rows per half-wave) and the
 // ds_read_b64_tr_b16 V-operand reads free of bank conflicts.  The pattern

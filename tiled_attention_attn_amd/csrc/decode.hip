@@ -12,7 +12,7 @@
 // fp32 workspace.  The combine kernel then merges the splits by their LSE.
 //
 // gfx950 mapping:
-//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 (16 keys x
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 / _f16 (16 keys x
 //    16 query rows per block); the S^T registers are the P^T operand
 //    directly, and V^T comes from LDS through ds_read_b64_tr_b16.
 //  * Page rows (256 bytes at D=128) are copied global -> LDS with
@@ -50,7 +50,7 @@ __device__ __forceinline__ uint32_t dec_tile_off(uint32_t row, uint32_t chunk) {
 
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(const DecParams p) {
   constexpr int kDecKBlk = DecKBlk<D>::value;
@@ -117,11 +117,11 @@ decode_kernel(const DecParams p) {
   }
 
   // Q^T fragments (B operand, k = head dim, n = row).
-  bf16x8 qf[NC];
+  vec8<T> qf[NC];
   {
-    const bf16* src = p.q + b * p.q_sb + hq * p.q_sh + (int64_t)t * p.q_sn + 8 * grp;
+    const T* src = static_cast<const T*>(p.q) + b * p.q_sb + hq * p.q_sh + (int64_t)t * p.q_sn + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 32 * c);
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const vec8<T>*>(src + 32 * c);
   }
   // The split's block-table entries go to LDS once, so the pipelined loop
   // below issues no vector-memory loads other than the K/V copies.
@@ -150,8 +150,8 @@ decode_kernel(const DecParams p) {
       const int page = s_pages[pidx];
       const int64_t off = ((int64_t)page * p.ps + key % p.ps) * row_stride + kvh * D + chunk * 8;
       const uint32_t loff = __builtin_amdgcn_readfirstlane(inst * 1024);
-      dma16(p.kc + off, lds_addr(bufK(st)) + loff);
-      dma16(p.vc + off, lds_addr(bufV(st)) + loff);
+      dma16(static_cast<const T*>(p.kc) + off, lds_addr(bufK(st)) + loff);
+      dma16(static_cast<const T*>(p.vc) + off, lds_addr(bufV(st)) + loff);
     }
   };
   constexpr int LOADS = 2 * PER_WAVE;  // copies per wave per step
@@ -183,7 +183,7 @@ decode_kernel(const DecParams p) {
       const uint32_t row = 16 * kb16 + col;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sacc[kb16] = mfma16(lds_read_b128(tK, dec_tile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
+        sacc[kb16] = mfma16(lds_read_b128<T>(tK, dec_tile_off<D>(row, 4 * c + grp)), qf[c], sacc[kb16]);
     }
     const bool full = kb >= wlo && kb + kDecKBlk - 1 <= whi;
     if (!full) {
@@ -209,7 +209,7 @@ decode_kernel(const DecParams p) {
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
-    bf16x8 pf[NKC];
+    vec8<T> pf[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       float e[8];
@@ -218,7 +218,7 @@ decode_kernel(const DecParams p) {
         e[i] = fast_exp2(__builtin_fmaf(sacc[2 * kc + (i >> 2)][i & 3], p.c2, -m_use));
         l_run += e[i];
       }
-      pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pf[kc] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -230,7 +230,7 @@ decode_kernel(const DecParams p) {
         const uint32_t sub = 8 * (col & 1);
         const i16x4 v0 = lds_read_tr16(tV, dec_tile_off<D>(r1, dcol >> 3) + sub);
         const i16x4 v1 = lds_read_tr16(tV, dec_tile_off<D>(r2, dcol >> 3) + sub);
-        oacc[db] = mfma16(join_tr(v0, v1), pf[kc], oacc[db]);
+        oacc[db] = mfma16(join_tr<T>(v0, v1), pf[kc], oacc[db]);
       }
     }
   }
@@ -257,12 +257,13 @@ decode_kernel(const DecParams p) {
 // so all of a row's loads are in flight together; a lane's float4s share one
 // d-slice because D/4 divides 64, and the lanes holding the same d-slice are
 // summed with cross-lane adds at the end.
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ ws_o,
                                                       const float* __restrict__ ws_lse,
                                                       int n_rows, int Hq, int Lq, int S,
-                                                      bf16* o, int64_t o_sb, int64_t o_sh,
+                                                      void* o_, int64_t o_sb, int64_t o_sh,
                                                       int64_t o_sn, float* lse) {
+  T* o = static_cast<T*>(o_);
   constexpr int Q4 = D / 4;  // float4s per split row
   static_assert(64 % Q4 == 0, "a lane's float4s must share one d-slice");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -292,31 +293,46 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
   const int t = row % Lq, bh = row / Lq, h = bh % Hq, b = bh / Hq;
   if (lane < Q4) {
-    bf16* dst = o + b * o_sb + h * o_sh + (int64_t)t * o_sn + 4 * lane;
-    const bf16x2 lo2 = pack2(acc[0], acc[1]), hi2 = pack2(acc[2], acc[3]);
-    *reinterpret_cast<bf16x4*>(dst) = bf16x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    T* dst = o + b * o_sb + h * o_sh + (int64_t)t * o_sn + 4 * lane;
+    *reinterpret_cast<vec4<T>*>(dst) = pack4<T>(acc[0], acc[1], acc[2], acc[3]);
   }
   if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m_use + logf(tot) : kNegInf;
 }
 
-int launch_decode(const DecParams& p, int D, hipStream_t stream) {
+template <typename T>
+void launch_decode_t(const DecParams& p, int D, dim3 grid, dim3 block, hipStream_t stream) {
+  if (D == 64) hipLaunchKernelGGL((decode_kernel<64, T>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel<128, T>), grid, block, 0, stream, p);
+}
+
+int launch_decode(const DecParams& p, int D, int dtype, hipStream_t stream) {
   dim3 grid(p.S * p.n_rg, p.Hkv, p.B), block(kDecThreads);
-  if (D == 64) hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, stream, p);
+  if (dtype == ATTN_DTYPE_F16) launch_decode_t<f16>(p, D, grid, block, stream);
+  else launch_decode_t<bf16>(p, D, grid, block, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+template <typename T>
+void launch_combine_t(const float* ws_o, const float* ws_lse, int n_rows, int Hq, int Lq, int S,
+                      int D, void* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
+                      dim3 grid, dim3 block, hipStream_t stream) {
+  if (D == 64)
+    hipLaunchKernelGGL((combine_kernel<64, T>), grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq,
+                       Lq, S, o, o_sb, o_sh, o_sn, lse);
+  else
+    hipLaunchKernelGGL((combine_kernel<128, T>), grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq,
+                       Lq, S, o, o_sb, o_sh, o_sn, lse);
+}
+
 int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
-                   bf16* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
+                   int dtype, void* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
                    hipStream_t stream) {
   const int n_rows = B * Hq * Lq;
   dim3 grid((n_rows + 3) / 4), block(256);
-  if (D == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq, Lq,
-                       S, o, o_sb, o_sh, o_sn, lse);
+  if (dtype == ATTN_DTYPE_F16)
+    launch_combine_t<f16>(ws_o, ws_lse, n_rows, Hq, Lq, S, D, o, o_sb, o_sh, o_sn, lse, grid, block, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, stream, ws_o, ws_lse, n_rows, Hq, Lq,
-                       S, o, o_sb, o_sh, o_sn, lse);
+    launch_combine_t<bf16>(ws_o, ws_lse, n_rows, Hq, Lq, S, D, o, o_sb, o_sh, o_sn, lse, grid, block, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

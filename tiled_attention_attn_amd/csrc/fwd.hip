@@ -12,11 +12,11 @@
 // symmetric window) and explicit FULL / PARTIAL tile lists for BlockMask.
 //
 // gfx950 mapping:
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys are the M dimension,
-//    queries the N dimension), so each lane owns one query column and the row
-//    max / row sum are in-lane except for one exchange with lane l^32
-//    (v_permlane32_swap).
-//  * The S^T accumulator registers, converted to bf16, are directly the
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (_f16 for fp16 inputs; keys
+//    are the M dimension, queries the N dimension), so each lane owns one
+//    query column and the row max / row sum are in-lane except for one
+//    exchange with lane l^32 (v_permlane32_swap).
+//  * The S^T accumulator registers, converted to bf16 / fp16, are directly the
 //    B operand of O^T += V^T P^T: the order of the 16 keys inside each PV
 //    MFMA is permuted the same way on the V side, which needs no shuffle.
 //  * V^T operands come from LDS with ds_read_b64_tr_b16 (transposing loads);
@@ -53,7 +53,7 @@ struct Step {
   int use_row_interval;  // 1: the row's own mask interval; 0: only k < Nk
 };
 
-template <int D, bool BM, int NST>
+template <int D, bool BM, int NST, typename T>
 __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
                                              int b, int h, int kvh) {
   constexpr int kKBlk = KBlk<D>::value;
@@ -72,9 +72,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5;
 
-  const bf16* __restrict__ Qbh = p.q + b * p.q_sb + h * p.q_sh;
-  const bf16* __restrict__ Kbh = p.k + b * p.k_sb + kvh * p.k_sh;
-  const bf16* __restrict__ Vbh = p.v + b * p.v_sb + kvh * p.v_sh;
+  const T* __restrict__ Qbh = static_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const T* __restrict__ Kbh = static_cast<const T*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const T* __restrict__ Vbh = static_cast<const T*>(p.v) + b * p.v_sb + kvh * p.v_sh;
 
   const int q0 = qt * kQTile;
   const int qrow = q0 + wave * 32 + (lane & 31);
@@ -82,12 +82,12 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   const int64_t shift = (int64_t)p.Nk - p.Nq;
 
   // Q^T fragments: B operand of S^T = K Q^T (k = head dim, n = query).
-  bf16x8 qf[NC];
+  vec8<T> qf[NC];
   {
     const int r = row_ok ? qrow : p.Nq - 1;
-    const bf16* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
+    const T* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const vec8<T>*>(src + 16 * c);
     // Complete these loads here, so the waits inside the step loop only ever
     // concern the asynchronous K/V copies.
     wait_vmem();
@@ -179,8 +179,8 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     int kb = step_at(s).kb;
     kb = kb < 0 ? 0 : (kb > p.Nk - 1 ? p.Nk - 1 : kb);
     const uint32_t lk = lds_addr(smem) + stage * STAGE_BYTES;
-    const bf16* kbase = Kbh + (int64_t)kb * p.k_sn;
-    const bf16* vbase = Vbh + (int64_t)kb * p.v_sn;
+    const T* kbase = Kbh + (int64_t)kb * p.k_sn;
+    const T* vbase = Vbh + (int64_t)kb * p.v_sn;
     if (kb + kKBlk <= p.Nk) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
@@ -224,7 +224,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       sacc[kbk] = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8 kf = lds_read_b128(tK, k_addr[c] + kbk * 32 * 2 * D);
+        const vec8<T> kf = lds_read_b128<T>(tK, k_addr[c] + kbk * 32 * 2 * D);
         sacc[kbk] = mfma32(kf, qf[c], sacc[kbk]);
       }
     }
@@ -258,7 +258,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     // is taken again.  Each row is thus normalised against some value at most
     // kSumCap + log2(64) below its running max: the online softmax of
     // section 3.2 with the rescale deferred until it is needed.
-    bf16x8 pf[NKC];
+    vec8<T> pf[NKC];
     auto probs = [&](float m_use) -> float {
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -267,11 +267,11 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
-          // l sums the fp32 values: summing the bf16-rounded P instead would
+          // l sums the fp32 values: summing the rounded P instead would
           // put up to 2^-9 of relative error into LSE.
           if (i & 1) ps1 += e[i]; else ps0 += e[i];
         }
-        pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        pf[kc] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       }
       return ps0 + ps1;
     };
@@ -303,7 +303,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       for (int db = 0; db < NDB; ++db) {
         const i16x4 v0 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][0] + kc_off);
         const i16x4 v1 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][1] + kc_off);
-        oacc[db] = mfma32(join_tr(v0, v1), pf[kc], oacc[db]);
+        oacc[db] = mfma32(join_tr<T>(v0, v1), pf[kc], oacc[db]);
       }
     }
   };
@@ -322,15 +322,14 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
   const float l_tot = l_run + other_half(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* Orow = p.o + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_sn;
+    T* Orow = static_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x2 a = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
-        const bf16x2 c = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        const bf16x4 w = {a[0], a[1], c[0], c[1]};
-        *reinterpret_cast<bf16x4*>(Orow + 32 * db + 8 * r4 + 4 * half) = w;
+        *reinterpret_cast<vec4<T>*>(Orow + 32 * db + 8 * r4 + 4 * half) =
+            pack4<T>(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv,
+                     oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
       }
     if (p.lse != nullptr && half == 0)
       p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] =
@@ -342,7 +341,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
 // per wave each).
 template <int D> struct Occ { static constexpr int value = 2; };
 
-template <int D, bool BM>
+template <int D, bool BM, typename T>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<D>::value, Occ<D>::value)))
 fwd_kernel(const FwdParams p) {
   constexpr int NST = Stages<D>::value;
@@ -364,31 +363,38 @@ fwd_kernel(const FwdParams p) {
   r /= p.n_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  process_tile<D, BM, NST>(p, smem, slot, b, h, kvh);
+  process_tile<D, BM, NST, T>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      process_tile<D, BM, NST>(p, smem, qt2, b, h, kvh);
+      process_tile<D, BM, NST, T>(p, smem, qt2, b, h, kvh);
     }
   }
 }
 
-int launch_fwd_pp(const FwdParams& p, int D, hipStream_t stream);
+int launch_fwd_pp(const FwdParams& p, int D, int dtype, hipStream_t stream);
+
+template <typename T>
+void launch_fwd_t(const FwdParams& p, int D, bool blockmask, dim3 grid, dim3 block,
+                  hipStream_t stream) {
+  if (D == 64) {
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<64, true, T>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<64, false, T>), grid, block, 0, stream, p);
+  } else {
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<128, true, T>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<128, false, T>), grid, block, 0, stream, p);
+  }
+}
 
 // Dense masks at D=128 run on the two-group ping-pong kernel of fwd_pp.hip
 // (measured 5% faster there); D=64 and BlockMask lists run on fwd_kernel.
-int launch_fwd(const FwdParams& p, int D, bool blockmask, hipStream_t stream) {
-  if (!blockmask && D == 128) return launch_fwd_pp(p, D, stream);
+int launch_fwd(const FwdParams& p, int D, bool blockmask, int dtype, hipStream_t stream) {
+  if (!blockmask && D == 128) return launch_fwd_pp(p, D, dtype, stream);
   const long units = (long)p.B * p.Hq * p.n_slots;
   dim3 grid((unsigned)units), block(kThreads);
-  if (D == 64) {
-    if (blockmask) hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, stream, p);
-  } else {
-    if (blockmask) hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, stream, p);
-  }
+  if (dtype == ATTN_DTYPE_F16) launch_fwd_t<f16>(p, D, blockmask, grid, block, stream);
+  else launch_fwd_t<bf16>(p, D, blockmask, grid, block, stream);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -20,7 +20,7 @@
 //    global_load_lds_dwordx4 one stage (two phases) ahead of use; the 256
 //    query rows share every K/V byte copied.
 //  * MFMA layouts, the chunk swizzle and the deferred-rescale online softmax
-//    are those of fwd.hip: S^T on 32x32x16 bf16 MFMAs, P^T taken from the
+//    are those of fwd.hip: S^T on 32x32x16 bf16/fp16 MFMAs, P^T taken from the
 //    S^T accumulators, V^T read with ds_read_b64_tr_b16.
 //  * Each wave decides per step, from its own 32 rows' mask intervals,
 //    whether the step is invisible (skipped), fully visible, or needs the
@@ -40,7 +40,7 @@ template <int D> struct PPKBlk { static constexpr int value = D == 64 ? 128 : 64
 // A lane's partial row sum of P above 2^12 moves the reference max.
 constexpr float kPPSumCap = 4096.0f;
 
-template <int D>
+template <int D, typename T>
 __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem, int qt, int b,
                                         int h, int kvh) {
   constexpr int KB = PPKBlk<D>::value;
@@ -59,9 +59,9 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   const int grp = wave >> 2;
   const int half = lane >> 5;
 
-  const bf16* __restrict__ Qbh = p.q + b * p.q_sb + h * p.q_sh;
-  const bf16* __restrict__ Kbh = p.k + b * p.k_sb + kvh * p.k_sh;
-  const bf16* __restrict__ Vbh = p.v + b * p.v_sb + kvh * p.v_sh;
+  const T* __restrict__ Qbh = static_cast<const T*>(p.q) + b * p.q_sb + h * p.q_sh;
+  const T* __restrict__ Kbh = static_cast<const T*>(p.k) + b * p.k_sb + kvh * p.k_sh;
+  const T* __restrict__ Vbh = static_cast<const T*>(p.v) + b * p.v_sb + kvh * p.v_sh;
 
   const int q0 = qt * kPPRows;
   const int wq0 = q0 + wave * 32;  // this wave's first row
@@ -70,12 +70,12 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   const bool row_ok = qrow < p.Nq;
   const int64_t shift = (int64_t)p.Nk - p.Nq;
 
-  bf16x8 qf[NC];
+  vec8<T> qf[NC];
   {
     const int r = row_ok ? qrow : p.Nq - 1;
-    const bf16* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
+    const T* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(src + 16 * c);
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const vec8<T>*>(src + 16 * c);
     wait_vmem();  // the loop's waits then only concern the K/V copies
   }
   int lo, hi;
@@ -118,11 +118,11 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   // Rows of a step past the last key repeat the last key row, and a step
   // outside [0, Nk) reads the nearest in-range rows: every stage issues the
   // same copies per thread, so the vmcnt bookkeeping below is exact.
-  auto copy_tile = [&](const bf16* base_bh, int64_t sn, const uint32_t (&voff)[CPT], int j,
+  auto copy_tile = [&](const T* base_bh, int64_t sn, const uint32_t (&voff)[CPT], int j,
                        uint32_t lds) {
     int kb = kb_begin + j * KB;
     kb = kb < 0 ? 0 : (kb > p.Nk - 1 ? p.Nk - 1 : kb);
-    const bf16* src = base_bh + (int64_t)kb * sn;
+    const T* src = base_bh + (int64_t)kb * sn;
     const uint32_t last = (uint32_t)(p.Nk - 1 - kb);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -160,7 +160,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
   f32x16 sacc[NKB];  // S(j): written in M(j), read in V(j)
-  bf16x8 pf[NKC];    // P(j): written in V(j), read in M(j+1)
+  vec8<T> pf[NKC];    // P(j): written in V(j), read in M(j+1)
 
   // ---- MFMA phase M(j): O += V(j-1) P(j-1), then S(j) = K(j) Q^T ----
   auto mfma_phase = [&](int j) {
@@ -174,7 +174,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
         for (int db = 0; db < NDB; ++db) {
           const i16x4 v0 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][0] + kc_off);
           const i16x4 v1 = lds_read_tr16(tV, v_addr[kc % KC_PERIOD][db][1] + kc_off);
-          oacc[db] = mfma32(join_tr(v0, v1), pf[kc], oacc[db]);
+          oacc[db] = mfma32(join_tr<T>(v0, v1), pf[kc], oacc[db]);
         }
       }
       // Keep the transposing reads about four MFMAs ahead of their use.
@@ -193,7 +193,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
         sacc[kbk] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          sacc[kbk] = mfma32(lds_read_b128(tK, k_addr[c] + kbk * 32 * 2 * D), qf[c], sacc[kbk]);
+          sacc[kbk] = mfma32(lds_read_b128<T>(tK, k_addr[c] + kbk * 32 * 2 * D), qf[c], sacc[kbk]);
       }
       // Keep the K reads about four MFMAs ahead of their use.
       constexpr int NQK = NKB * NC;
@@ -218,7 +218,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
         e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
         if (i & 1) ps1 += e[i]; else ps0 += e[i];
       }
-      pf[kc] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pf[kc] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     return ps0 + ps1;
   };
@@ -307,15 +307,14 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   const float l_tot = l_run + other_half(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* Orow = p.o + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_sn;
+    T* Orow = static_cast<T*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const bf16x2 a = pack2(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv);
-        const bf16x2 c = pack2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-        const bf16x4 w = {a[0], a[1], c[0], c[1]};
-        *reinterpret_cast<bf16x4*>(Orow + 32 * db + 8 * r4 + 4 * half) = w;
+        *reinterpret_cast<vec4<T>*>(Orow + 32 * db + 8 * r4 + 4 * half) =
+            pack4<T>(oacc[db][4 * r4 + 0] * inv, oacc[db][4 * r4 + 1] * inv,
+                     oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
       }
     if (p.lse != nullptr && half == 0)
       p.lse[((int64_t)b * p.Hq + h) * p.Nq + qrow] =
@@ -323,7 +322,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   }
 }
 
-template <int D>
+template <int D, typename T>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pp_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kPPStages * 2 * PPKBlk<D>::value * D * 2];
@@ -343,12 +342,12 @@ fwd_pp_kernel(const FwdParams p) {
   r /= p.n_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  pp_tile<D>(p, smem, slot, b, h, kvh);
+  pp_tile<D, T>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      pp_tile<D>(p, smem, qt2, b, h, kvh);
+      pp_tile<D, T>(p, smem, qt2, b, h, kvh);
     }
   }
 }
@@ -357,7 +356,7 @@ fwd_pp_kernel(const FwdParams p) {
 
 // Dense-mask prefill on 256-row tiles.  `p` describes 128-row tiles; the
 // tile count, pairing and XCD mapping are recomputed here.
-int launch_fwd_pp(const FwdParams& p_in, int D, hipStream_t stream) {
+int launch_fwd_pp(const FwdParams& p_in, int D, int dtype, hipStream_t stream) {
   FwdParams p = p_in;
   p.n_qt = (p.Nq + kPPRows - 1) / kPPRows;
   p.paired = p_in.paired && p.n_qt > 1;
@@ -366,7 +365,8 @@ int launch_fwd_pp(const FwdParams& p_in, int D, hipStream_t stream) {
   p.xcd_remap = (units % 8) == 0;
   dim3 grid((unsigned)units), block(kPPThreads);
   if (D != 128) return ATTN_ERR_HEAD_DIM;  // D=64 prefill runs on fwd_kernel
-  hipLaunchKernelGGL(fwd_pp_kernel<128>, grid, block, 0, stream, p);
+  if (dtype == ATTN_DTYPE_F16) hipLaunchKernelGGL((fwd_pp_kernel<128, f16>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((fwd_pp_kernel<128, bf16>), grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

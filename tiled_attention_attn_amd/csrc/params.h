@@ -1,5 +1,7 @@
 // Kernel parameter blocks (passed by value to the kernels), shared by the
-// kernel sources and the host-side C ABI that fills them.
+// kernel sources and the host-side C ABI that fills them.  Tensor pointers
+// are untyped: each kernel is instantiated for its element type (bf16 or
+// fp16) and casts them.
 #pragma once
 
 #include "common.h"
@@ -8,10 +10,10 @@ namespace tattn {
 
 // Prefill (dense-mask and BlockMask variants).
 struct FwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  bf16* o;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
   float* lse;
   int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn, o_sb, o_sh, o_sn;
   int B, Hq, Hkv, G, Nq, Nk;
@@ -43,10 +45,10 @@ struct BmBuildParams {
 
 // Split-KV paged decode.
 struct DecParams {
-  const bf16* q;
+  const void* q;
   int64_t q_sb, q_sh, q_sn;
-  const bf16* kc;
-  const bf16* vc;
+  const void* kc;
+  const void* vc;
   const int32_t* bt;
   int64_t bt_stride;
   const int32_t* seq_lens;
@@ -62,15 +64,15 @@ struct DecParams {
 
 // Backward pass (dQ, dK, dV by recomputation).
 struct BwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  const bf16* o;
-  const bf16* dout;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
   const float* lse;
-  bf16* dq;
-  bf16* dk;
-  bf16* dv;
+  void* dq;
+  void* dk;
+  void* dv;
   int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn, o_sb, o_sh, o_sn;
   int64_t do_sb, do_sh, do_sn, dq_sb, dq_sh, dq_sn, dk_sb, dk_sh, dk_sn, dv_sb, dv_sh, dv_sn;
   int B, Hq, Hkv, G, Nq, Nk;

@@ -43,6 +43,11 @@ def randn_bf16(gen: torch.Generator, shape) -> torch.Tensor:
     return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
 
 
+def randn_half(gen: torch.Generator, shape, dtype=torch.bfloat16) -> torch.Tensor:
+    """fp32 N(0,1) draw rounded (RNE) to a 16-bit float type (bf16 or fp16), on the CPU."""
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(dtype)
+
+
 def doc_lengths(gen: torch.Generator, n: int, lo: int = 512, hi: int = 2048) -> list[int]:
     """Document lengths drawn uniform on the integers [lo, hi] until they cover n tokens."""
     out: list[int] = []
