@@ -26,13 +26,15 @@ Modules:
     blockmask  -- tile classes (EMPTY / PARTIAL / FULL) from a dense mask, and
                   the compacted per-row tile lists
     backward   -- dQ, dK, dV of the same definition (softmax Jacobian, chain rule)
+    score_mods -- additive score modifications: ALiBi, symmetric ALiBi, a
+                  relative-position bias table (FlexAttention article, section 1)
 
 Every function is pinned by CPU tests (brute force on tiny inputs, torch's
 float64 CPU scaled_dot_product_attention, closed forms, invariants and
 identities); no function here is "parity unpinned".
 """
-from . import masks, core, paged, blockmask, backward
+from . import masks, core, paged, blockmask, backward, score_mods
 from .core import attention, attention_rows, combine, scores, masked_softmax
 
-__all__ = ["masks", "core", "paged", "blockmask", "backward", "attention", "attention_rows", "combine",
+__all__ = ["masks", "core", "paged", "blockmask", "backward", "score_mods", "attention", "attention_rows", "combine",
            "scores", "masked_softmax"]

@@ -17,6 +17,11 @@ with the softmax Jacobian taken row by row:
     dS = P * (dP - rowsum(P * dP))
     dQ = scale * dS K,     dK = scale * dS^T Q
 
+With an additive score_mod (oracle.score_mods: the modified score is
+s + bias(h, q, k)) P is the softmax of the modified scores and, since
+d(s + bias)/ds = 1, the formulas above are unchanged; the bias itself gets no
+gradient here.
+
 GQA (query head hq reads KV head hq // G): dK and dV of a KV head sum the
 contributions of all G query heads that read it.  A row with no visible key
 has P = 0 and contributes nothing.  No tiling, no recomputation order: the
@@ -35,6 +40,7 @@ import numpy as np
 
 from . import core as _core
 from . import masks as _masks
+from . import score_mods as _score_mods
 
 
 def softmax_grad(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
@@ -42,7 +48,7 @@ def softmax_grad(p: np.ndarray, dp: np.ndarray) -> np.ndarray:
     return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
 
 
-def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows):
+def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows, score_mod=None):
     """For query rows ``rows`` of (b, hq): (dQ rows, dK part, dV part, P, dS).
 
     dK part / dV part are this row block's contributions to the gradients of
@@ -57,6 +63,8 @@ def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows):
     kk = np.asarray(k[b, kvh], dtype=np.float64)
     vv = np.asarray(v[b, kvh], dtype=np.float64)
     s = _core.scores(qr, kk, scale)
+    if score_mod is not None:
+        s = _score_mods.dense(score_mod, b, hq, s, rows, Nk)
     if mask_mod is None:
         vis = np.ones_like(s, dtype=bool)
     else:
@@ -68,7 +76,7 @@ def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows):
 
 
 def attention_bwd(q, k, v, do, scale: float | None = None, mask_mod=None, row_block: int = 512,
-                  bound: bool = False, o_used=None):
+                  bound: bool = False, o_used=None, score_mod=None):
     """dQ [B, Hq, Nq, D], dK and dV [B, Hkv, Nk, D] in float64.
 
     With ``bound``, also (mQ, mK, mV) of the same shapes: mV = sum_q P |dO|,
@@ -90,7 +98,7 @@ def attention_bwd(q, k, v, do, scale: float | None = None, mask_mod=None, row_bl
             kvh = h // G
             for r0 in range(0, Nq, row_block):
                 rows = np.arange(r0, min(Nq, r0 + row_block))
-                dqr, dkp, dvp, p, ds = bwd_rows(q, k, v, do, scale, mask_mod, b, h, rows)
+                dqr, dkp, dvp, p, ds = bwd_rows(q, k, v, do, scale, mask_mod, b, h, rows, score_mod)
                 dq[b, h, rows] = dqr
                 dk[b, kvh] += dkp
                 dv[b, kvh] += dvp

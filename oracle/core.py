@@ -20,6 +20,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import masks as _masks
+from . import score_mods as _score_mods
 
 
 def scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
@@ -42,10 +43,12 @@ def masked_softmax(s: np.ndarray, visible: np.ndarray):
     return p, lse[..., 0]
 
 
-def attention_rows(q, k, v, scale: float, mask_mod, b: int, hq: int, rows):
+def attention_rows(q, k, v, scale: float, mask_mod, b: int, hq: int, rows, score_mod=None):
     """O [len(rows), D] and LSE [len(rows)] for query rows ``rows`` of (b, hq).
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]; any float dtype (upcast exactly).
+    ``score_mod`` (oracle.score_mods) changes the scaled scores before the
+    softmax; LSE is then the log-sum-exp of the changed scores.
     """
     Hq, Nq = q.shape[1], q.shape[2]
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -57,6 +60,8 @@ def attention_rows(q, k, v, scale: float, mask_mod, b: int, hq: int, rows):
     kk = np.asarray(k[b, kvh], dtype=np.float64)
     vv = np.asarray(v[b, kvh], dtype=np.float64)
     s = scores(qr, kk, scale)
+    if score_mod is not None:
+        s = _score_mods.dense(score_mod, b, hq, s, rows, Nk)
     if mask_mod is None:
         vis = np.ones_like(s, dtype=bool)
     else:
@@ -65,7 +70,8 @@ def attention_rows(q, k, v, scale: float, mask_mod, b: int, hq: int, rows):
     return p @ vv, lse
 
 
-def attention(q, k, v, scale: float | None = None, mask_mod=None, row_block: int = 512):
+def attention(q, k, v, scale: float | None = None, mask_mod=None, row_block: int = 512,
+              score_mod=None):
     """Full O [B, Hq, Nq, D] and LSE [B, Hq, Nq] in float64."""
     B, Hq, Nq, D = q.shape
     if scale is None:
@@ -76,7 +82,8 @@ def attention(q, k, v, scale: float | None = None, mask_mod=None, row_block: int
         for h in range(Hq):
             for r0 in range(0, Nq, row_block):
                 rows = np.arange(r0, min(Nq, r0 + row_block))
-                o[b, h, rows], lse[b, h, rows] = attention_rows(q, k, v, scale, mask_mod, b, h, rows)
+                o[b, h, rows], lse[b, h, rows] = attention_rows(q, k, v, scale, mask_mod, b, h, rows,
+                                                                score_mod)
     return o, lse
 
 

@@ -56,8 +56,32 @@ def _range_keys(spec, q, Nq, Nk):
     return sorted(keys)
 
 
-def attention(q, k, v, scale, spec):
-    """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) nested lists."""
+def _bias(score_spec, h, j, p):
+    """Additive score change for query head h, key j, query position p."""
+    if not score_spec:
+        return 0.0
+    add = 0.0
+    if "alibi" in score_spec:
+        add += score_spec["alibi"][h] * (j - p)
+    if "alibi_sym" in score_spec:
+        add -= score_spec["alibi_sym"][h] * abs(j - p)
+    if "rel" in score_spec:
+        table, R = score_spec["rel"]
+        d = j - p
+        if d < -R:
+            d = -R
+        if d > R:
+            d = R
+        add += table[h][d + R]
+    return add
+
+
+def attention(q, k, v, scale, spec, score_spec=None):
+    """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) nested lists.
+
+    score_spec (optional) adds to each scaled score: "alibi": slopes per head
+    (+ slope (j - p)), "alibi_sym": slopes (- slope |j - p|), "rel": (table, R)
+    (+ table[h][clamp(j - p, -R, R) + R])."""
     B, Hq = len(q), len(q[0])
     Hkv = len(k[0])
     Nq, Nk = len(q[0][0]), len(k[0][0])
@@ -75,7 +99,9 @@ def attention(q, k, v, scale, spec):
                     Oh.append([0.0] * dv)
                     Lh.append(-math.inf)
                     continue
-                s = {j: scale * math.fsum(a * c for a, c in zip(q[b][h][i], k[b][kv][j])) for j in keys}
+                pos = i + (Nk - Nq)
+                s = {j: scale * math.fsum(a * c for a, c in zip(q[b][h][i], k[b][kv][j]))
+                     + _bias(score_spec, h, j, pos) for j in keys}
                 m = max(s.values())
                 e = {j: math.exp(s[j] - m) for j in keys}
                 tot = math.fsum(e.values())

@@ -12,6 +12,8 @@ import oracle
 from oracle import core as OA, masks as M, paged as OP, blockmask as OB, backward as OBW
 import test_oracle_pins as P
 import test_oracle_backward as PB
+import test_oracle_score_mods as PS
+from oracle import score_mods as OSM
 
 PINS = [
     lambda: [P.pin_brute(c) for c in P.BRUTE_CASES],
@@ -19,7 +21,7 @@ PINS = [
     P.pin_sdpa_decode_paged, P.pin_probs_sum_to_one, P.pin_constant_v, P.pin_one_visible_key,
     P.pin_q0_counts, P.pin_identities, P.pin_split_combine, P.pin_paged_equals_contiguous,
     P.pin_blockmask_classes, P.test_hand_worked_golden, P.test_brute_force_paged_two_splits,
-] + PB.BWD_PINS
+] + PB.BWD_PINS + PS.SCORE_PINS
 
 
 def _caught():
@@ -150,6 +152,48 @@ def _bwd_rows_gqa_modulo(q, k, v, do, scale, mask_mod, b, hq, rows):
     kk[:, kvh], vv[:, kvh] = np.asarray(k)[:, hq % Hkv], np.asarray(v)[:, hq % Hkv]
     return _orig_bwd_rows(q, kk, vv, do, scale, mask_mod, b, hq, rows)
 
+def _alibi_sign(slopes, Nq, Nk):
+    sl = np.asarray(slopes, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        return score - sl[h] * (np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq)))
+    return mod
+
+
+def _alibi_sym_no_abs(slopes, Nq, Nk):
+    sl = np.asarray(slopes, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        return score - sl[h] * (np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq)))
+    return mod
+
+
+def _alibi_top_left(slopes, Nq, Nk):
+    sl = np.asarray(slopes, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        return score + sl[h] * (np.asarray(kv_idx) - np.asarray(q_idx))
+    return mod
+
+
+def _rel_bias_unclamped_offset(table, R, Nq, Nk):
+    tb = np.asarray(table, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        d = np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq))
+        return score + tb[h][np.clip(d + R, 0, 2 * R - 1)]
+    return mod
+
+
+def _rel_bias_reversed(table, R, Nq, Nk):
+    tb = np.asarray(table, dtype=np.float64)
+
+    def mod(score, b, h, q_idx, kv_idx):
+        d = np.asarray(q_idx) + (Nk - Nq) - np.asarray(kv_idx)
+        return score + tb[h][np.clip(d, -R, R) + R]
+    return mod
+
+
 MUTANTS = {
     "scale_dropped": (OA, "scores", _scores_no_scale),
     "lse_without_max": (OA, "masked_softmax", _softmax_lse_no_max),
@@ -169,6 +213,11 @@ MUTANTS = {
     "bwd_dq_uses_v": (OBW, "bwd_rows", _bwd_rows_dq_uses_v),
     "bwd_dv_from_o": (OBW, "bwd_rows", _bwd_rows_dv_from_o),
     "bwd_gqa_modulo_mapping": (OBW, "bwd_rows", _bwd_rows_gqa_modulo),
+    "alibi_sign": (OSM, "alibi", _alibi_sign),
+    "alibi_sym_without_abs": (OSM, "alibi_sym", _alibi_sym_no_abs),
+    "alibi_top_left": (OSM, "alibi", _alibi_top_left),
+    "rel_bias_clamp_off_by_one": (OSM, "rel_bias", _rel_bias_unclamped_offset),
+    "rel_bias_reversed_distance": (OSM, "rel_bias", _rel_bias_reversed),
 }
 
 
