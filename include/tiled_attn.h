@@ -71,6 +71,7 @@ extern "C" {
 #define ATTN_ERR_BLOCKMASK (-10)/* BlockMask descriptor inconsistent           */
 #define ATTN_ERR_SCALE (-11)    /* scale not finite and > 0                    */
 #define ATTN_ERR_DTYPE (-12)    /* dtype is not ATTN_DTYPE_BF16 / ATTN_DTYPE_F16 */
+#define ATTN_ERR_SCORE_MOD (-13)/* bad score_mod flags / parameters, or not supported here */
 
 /* ---- element types ------------------------------------------------------ */
 #define ATTN_DTYPE_BF16 0
@@ -107,12 +108,39 @@ typedef struct attn_mask_desc {
   int32_t doc_stride;   /* elements between rows of doc_offsets (>= num_docs + 1)  */
 } attn_mask_desc;
 
+/* ---- score modification -------------------------------------------------
+ * Additive changes of the scaled score before the softmax, the score_mod of
+ * the FlexAttention article (section 1: ALiBi, a position bias, a learnable
+ * bias).  With d = k - p (key index minus the query's aligned position):
+ *     ALIBI      score + slopes[hq] * d          (<= 0 where k <= p)
+ *     ALIBI_SYM  score - slopes[hq] * |d|
+ *     REL_BIAS   score + rel_bias[hq][clamp(d, -R, R) + R]
+ * ALIBI and ALIBI_SYM exclude each other; REL_BIAS combines with either.
+ * LSE is then the log-sum-exp of the changed scores.  The bias arrays are
+ * device memory; the backward pass treats them as constants (no gradient).
+ * REL_BIAS needs 0 <= R <= 1023 and, in attn_bwd, (Hq / Hkv) * (2R + 1) <=
+ * 8192; attn_decode_splitkv takes ALIBI / ALIBI_SYM only.  attn_fwd,
+ * attn_fwd_blockmask and attn_bwd take a score change at D = 128 only
+ * (ATTN_ERR_SCORE_MOD at D = 64).
+ */
+#define ATTN_SCORE_ALIBI 1u
+#define ATTN_SCORE_ALIBI_SYM 2u
+#define ATTN_SCORE_REL_BIAS 4u
+#define ATTN_SCORE_ALL 7u
+
+typedef struct attn_score_mod {
+  uint32_t flags;         /* ATTN_SCORE_* bits (0 = no change)                    */
+  const float* slopes;    /* ALIBI / ALIBI_SYM: device float [Hq]                 */
+  const float* rel_bias;  /* REL_BIAS: device float [Hq][2 * rel_radius + 1]      */
+  int32_t rel_radius;     /* REL_BIAS: R                                          */
+} attn_score_mod;
+
 /* ---- dense-mask prefill ---------------------------------------------------
  * attn_fwd: O = softmax(scale * Q K^T restricted by `mask`) V, plus LSE.
  *   q  [B, Hq,  Nq, D], k/v [B, Hkv, Nk, D], o [B, Hq, Nq, D] (strides (b,h,n))
  *   lse float [B, Hq, Nq] contiguous, or NULL.
- *   mask may be NULL (no mask).  Nq or Nk may be 0 (Nk = 0: every row empty;
- *   k and v may then be NULL).
+ *   mask may be NULL (no mask); smod may be NULL (no score change).  Nq or Nk
+ *   may be 0 (Nk = 0: every row empty; k and v may then be NULL).
  * The key blocks of a query block are chosen analytically from the mask's
  * per-row intervals: blocks outside every row's interval are skipped, blocks
  * inside every row's interval run unmasked, the rest apply the interval
@@ -123,7 +151,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3],
              const void* v, const int64_t v_stride[3],
              void* o, const int64_t o_stride[3], float* lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
-             const attn_mask_desc* mask, hipStream_t stream);
+             const attn_mask_desc* mask, const attn_score_mod* smod, hipStream_t stream);
 
 /* ---- BlockMask -----------------------------------------------------------
  * Block-level sparsity over 128 x 128 tiles (FlexAttention article,
@@ -175,8 +203,8 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3],
                        const void* v, const int64_t v_stride[3],
                        void* o, const int64_t o_stride[3], float* lse,
                        int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
-                       const attn_mask_desc* mask, const attn_blockmask* bm,
-                       hipStream_t stream);
+                       const attn_mask_desc* mask, const attn_score_mod* smod,
+                       const attn_blockmask* bm, hipStream_t stream);
 
 /* ---- split-KV paged decode -------------------------------------------------
  * "Short query, long KV" decoding split over the key sequence and merged by
@@ -212,7 +240,8 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3],
                         const int32_t* seq_lens, int max_pages,
                         int B, int Hq, int Hkv, int Lq, int D, int dtype, int page_size,
                         int num_splits, float scale, const attn_mask_desc* mask,
-                        float* ws_o, float* ws_lse, hipStream_t stream);
+                        const attn_score_mod* smod, float* ws_o, float* ws_lse,
+                        hipStream_t stream);
 
 /* attn_decode_combine: O = sum_s exp(LSE_s - LSE) O_s with
  * LSE = log sum_s exp(LSE_s) (max-shifted); splits with LSE_s = -inf weigh 0.
@@ -264,8 +293,8 @@ int attn_bwd(const void* q, const int64_t q_stride[3],
              void* dk, const int64_t dk_stride[3],
              void* dv, const int64_t dv_stride[3],
              int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
-             const attn_mask_desc* mask, float* workspace, size_t workspace_bytes,
-             hipStream_t stream);
+             const attn_mask_desc* mask, const attn_score_mod* smod,
+             float* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_str(int status);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(T):
 
 def test_status_strings(T):
     assert T.attn_status_str(0) == "ok"
-    for code in range(-12, 0):
+    for code in range(-13, 0):
         assert T.attn_status_str(code) != "unknown status"
     assert T.attn_abi_version() >= 1
 
@@ -51,13 +51,14 @@ def _strides(*v):
 def _fwd(T, **kw):
     lib = T.lib_handle()
     a = dict(q=16, k=32, v=48, o=64, qs=(64 * 256, 64 * 256, 64), ks=None, vs=None, os=None, lse=None,
-             B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, dtype=0, scale=0.125, mask=None)
+             B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, dtype=0, scale=0.125, mask=None, smod=None)
     a.update(kw)
     s = lambda x: _strides(*(x or a["qs"]))
     mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+    sm = None if a["smod"] is None else ctypes.byref(a["smod"])
     return lib.attn_fwd(a["q"], s(a["qs"]), a["k"], s(a["ks"]), a["v"], s(a["vs"]), a["o"], s(a["os"]),
                         a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], a["dtype"], a["scale"],
-                        mk, None)
+                        mk, sm, None)
 
 
 def test_fwd_argument_errors(T):
@@ -66,6 +67,17 @@ def test_fwd_argument_errors(T):
     assert _fwd(T, k=None) == -1
     assert _fwd(T, D=96) == -3
     assert _fwd(T, dtype=2) == -12 and _fwd(T, dtype=-1) == -12
+    SMD = T.attn_score_mod
+    qs128 = (128 * 256, 128 * 256, 128)
+    f128 = lambda **kw: _fwd(T, D=128, qs=qs128, **kw)
+    assert f128(smod=SMD(flags=8)) == -13                                    # unknown flag
+    assert f128(smod=SMD(flags=3, slopes=16)) == -13                         # ALIBI and ALIBI_SYM
+    assert f128(smod=SMD(flags=1, slopes=None)) == -1
+    assert f128(smod=SMD(flags=4, rel_bias=None, rel_radius=3)) == -1
+    assert f128(smod=SMD(flags=4, rel_bias=16, rel_radius=1024)) == -13     # 2R+1 > 2048
+    assert f128(smod=SMD(flags=4, rel_bias=16, rel_radius=-1)) == -13
+    assert _fwd(T, smod=SMD(flags=1, slopes=16)) == -13                      # D = 64 takes no score change
+    assert f128(smod=SMD(flags=0), B=0) == 0
     assert _fwd(T, Hq=3, Hkv=2) == -4
     assert _fwd(T, Hkv=0) == -4
     assert _fwd(T, qs=(64 * 256, 64 * 256, 60)) == -5
@@ -103,19 +115,21 @@ def test_blockmask_and_decode_argument_errors(T):
     qs = _strides(32 * 16 * 128, 16 * 128, 128)
     args = lambda **kw: dict(dict(q=16, qs=qs, kc=32, vc=48, pages=10, bt=64, bts=4, sl=80, maxp=4, B=1,
                                   Hq=4, Hkv=2, Lq=2, D=128, dt=0, ps=16, S=2, scale=0.1, mask=None, wo=96,
-                                  wl=112), **kw)
+                                  wl=112, smod=None), **kw)
 
     def dec(**kw):
         a = args(**kw)
         mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+        sm = None if a["smod"] is None else ctypes.byref(a["smod"])
         return lib.attn_decode_splitkv(a["q"], a["qs"], a["kc"], a["vc"], a["pages"], a["bt"], a["bts"],
                                        a["sl"], a["maxp"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"],
-                                       a["dt"], a["ps"], a["S"], a["scale"], mk, a["wo"], a["wl"], None)
+                                       a["dt"], a["ps"], a["S"], a["scale"], mk, sm, a["wo"], a["wl"], None)
     assert dec(wo=None) == -1
     assert dec(S=0) == -8
     assert dec(bts=3) == -2
     assert dec(D=80) == -3
     assert dec(dt=5) == -12
+    assert dec(smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=2)) == -13  # no table in decode
     assert dec(Hq=3) == -4
     md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=1, doc_stride=2)
     assert dec(mask=md) == -7
@@ -138,19 +152,25 @@ def test_bwd_argument_errors(T):
 
     def bwd(**kw):
         a = dict(q=16, k=32, v=48, o=64, do=80, lse=96, dq=112, dk=128, dv=144, s=qs, ks=qs, B=1, Hq=1,
-                 Hkv=1, Nq=256, Nk=256, D=64, dt=1, scale=0.125, mask=None, ws=160, wsb=ws)
+                 Hkv=1, Nq=256, Nk=256, D=64, dt=1, scale=0.125, mask=None, ws=160, wsb=ws, smod=None)
         a.update(kw)
         mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+        sm = None if a["smod"] is None else ctypes.byref(a["smod"])
         s, ks = a["s"], a["ks"]
         return lib.attn_bwd(a["q"], s, a["k"], ks, a["v"], s, a["o"], s, a["do"], s, a["lse"], a["dq"], s,
                             a["dk"], s, a["dv"], s, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"],
-                            a["dt"], a["scale"], mk, a["ws"], a["wsb"], None)
+                            a["dt"], a["scale"], mk, sm, a["ws"], a["wsb"], None)
     assert bwd(do=None) == -1
     assert bwd(lse=None) == -1
     assert bwd(dk=None) == -1
     assert bwd(ws=None) == -1
     assert bwd(D=32) == -3
     assert bwd(dt=7) == -12
+    # G (2R + 1) bias-table floats over 8192 for one work group
+    q128 = _strides(128 * 256, 128 * 256, 128)
+    assert bwd(D=128, s=q128, ks=q128, Hq=8, Hkv=1,
+               smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=512)) == -13
+    assert bwd(smod=T.attn_score_mod(flags=1, slopes=16)) == -13      # D = 64 takes no score change
     assert bwd(Hq=2, Hkv=3) == -4
     assert bwd(s=_strides(64 * 256, 64 * 256, 68)) == -5
     assert bwd(ks=_strides(1 << 30, 1 << 30, 1 << 24)) == -5  # streamed row stride over 2^24

@@ -1,0 +1,222 @@
+"""GPU parity: additive score changes (ALiBi, symmetric ALiBi, relative-position
+bias table) in prefill, BlockMask prefill, paged decode and the backward pass,
+against the fp64 oracle with the same score_mod."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward as OBW, masks as M, paged as OP, score_mods as SM
+import workloads as W
+from gpu_util import f64, assert_close, announce
+from test_gpu_prefill import _mask_pair
+from test_gpu_backward import _fwd_bwd, assert_grad_close
+
+pytestmark = pytest.mark.gpu
+
+# The prefill and backward kernels at D = 64 are not offered with a score
+# change: a run of these tests faulted the GPU in the D = 64 backward case
+# (symmetric ALiBi + bias table under a window mask) and no cause has been
+# shown yet, so the library rejects D = 64 score changes (ATTN_ERR_SCORE_MOD)
+# and their GPU cases are skipped until one is.
+D64_OFF = "score changes at D=64 are switched off after an unexplained GPU fault"
+
+if torch.cuda.is_available():  # the HIP library must load on a GPU machine: no fallback
+    import tiled_attention_attn_amd as T
+DEV = "cuda"
+
+
+def alibi_slopes(H):
+    """The geometric slopes 2^(-8 (h+1) / H) of the ALiBi recipe."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+
+
+def _smod_pair(kind, Hq, Nq, Nk, R=64, seed=0):
+    """(GPU ScoreMod, oracle score_mod, tensors kept alive) for a kind string."""
+    mods, keep, gm = [], [], T.ScoreMod()
+    if "alibi" in kind:
+        sl = alibi_slopes(Hq)
+        keep.append(sl.to(DEV))
+        gm.alibi_slopes = keep[-1]
+        gm.symmetric = "sym" in kind
+        mods.append((SM.alibi_sym if gm.symmetric else SM.alibi)(sl.double().numpy(), Nq, Nk))
+    if "rel" in kind:
+        g = torch.Generator().manual_seed(seed + 99)
+        tb = (0.5 * torch.randn(Hq, 2 * R + 1, generator=g)).float()
+        keep.append(tb.to(DEV))
+        gm.rel_bias = keep[-1]
+        mods.append(SM.rel_bias(tb.double().numpy(), R, Nq, Nk))
+    return gm, SM.combine(*mods), keep
+
+
+PREFILL = [
+    # (id, B, Hq, Hkv, Nq, Nk, D, mask spec, score kind)
+    ("alibi_causal_d64_gqa", 1, 4, 2, 700, 700, 64, {"causal": True}, "alibi"),
+    ("alibi_causal_d128", 1, 2, 2, 600, 600, 128, {"causal": True}, "alibi"),
+    ("alibi_sym_window_d128", 1, 2, 2, 777, 777, 128, {"window": (100, 100)}, "alibi_sym"),
+    ("rel_nomask_d64", 1, 2, 1, 300, 300, 64, {}, "rel"),
+    ("rel_alibi_sym_docs_d128", 2, 2, 2, 520, 520, 128, {"docs": [[130, 250, 140], [520]]}, "alibi_sym+rel"),
+    ("alibi_bottom_right_d64", 1, 2, 2, 100, 500, 64, {"causal": True}, "alibi"),
+    ("rel_causal_d128_ragged", 1, 2, 1, 333, 333, 128, {"causal": True}, "rel"),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
+def test_prefill_score_mod(case, dtype):
+    name, B, Hq, Hkv, Nq, Nk, D, mspec, kind = case
+    if D == 64:
+        pytest.skip(D64_OFF)
+    if dtype == torch.float16 and name not in ("alibi_causal_d128", "rel_alibi_sym_docs_d128"):
+        pytest.skip("fp16 checked on a subset")
+    announce(f"score_mod prefill {name} {dtype}")
+    g = W.generator(zlib.crc32(name.encode()) % 9973)
+    q = W.randn_half(g, (B, Hq, Nq, D), dtype)
+    k = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    v = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    scale = 1.0 / math.sqrt(D)
+    gm, mod = _mask_pair(mspec, B, Nq, Nk)
+    sg, smod, keep = _smod_pair(kind, Hq, Nq, Nk, R=48, seed=len(name))
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.full_like(qg, float("nan"))
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device=DEV)
+    T.attn_fwd(qg, kg, vg, o, lse, scale, gm, smod=sg)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod, score_mod=smod)
+    assert_close(f64(o), f64(lse), ro, rl, name)
+
+
+def test_d64_score_change_rejected():
+    """D = 64 prefill / backward calls with a score change fail on the host, before any launch."""
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=DEV)
+    sg = T.ScoreMod(alibi_slopes=alibi_slopes(2).to(DEV))
+    with pytest.raises(T.AttnError) as e:
+        T.attn_fwd(q, q, q, torch.empty_like(q), None, 0.125, None, smod=sg)
+    assert e.value.status == -13
+
+
+def test_blockmask_score_mod():
+    announce("score_mod blockmask")
+    D, Hq, Hkv, N = 128, 4, 2, 900
+    g = W.generator(77)
+    q = W.randn_bf16(g, (1, Hq, N, D))
+    k = W.randn_bf16(g, (1, Hkv, N, D))
+    v = W.randn_bf16(g, (1, Hkv, N, D))
+    nt = (N + 127) // 128
+    tm = W.blockmask_tile_map(g, nt, 0.3)
+    bm = T.BlockMask(1, 1, N, N)
+    T.attn_build_blockmask(bm, 1, N, N, tile_map=tm[None, None].contiguous().to(DEV))
+    sg, smod, keep = _smod_pair("alibi+rel", Hq, N, N, R=100, seed=3)
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.empty_like(qg)
+    lse = torch.empty(1, Hq, N, dtype=torch.float32, device=DEV)
+    T.attn_fwd_blockmask(qg, kg, vg, o, bm, lse, 1 / math.sqrt(D), T.Mask(causal=True), smod=sg)
+    torch.cuda.synchronize()
+    mod = M.blockmask(tm.numpy(), 128, M.causal(N, N))
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), 1 / math.sqrt(D), mod, score_mod=smod)
+    assert_close(f64(o), f64(lse), ro, rl, "blockmask score_mod")
+
+
+def test_alibi_closed_form_q0():
+    """Q = 0: every score is the ALiBi bias, so row p's LSE is the geometric sum
+    log((1 - e^{-a(p+1)}) / (1 - e^{-a})) (natural units), to fp32 accuracy."""
+    announce("score_mod closed form")
+    N, D, H = 1000, 128, 2
+    q = torch.zeros(1, H, N, D, dtype=torch.bfloat16)
+    g = W.generator(8)
+    k = W.randn_bf16(g, (1, H, N, D))
+    v = W.randn_bf16(g, (1, H, N, D))
+    sl = alibi_slopes(H)
+    sg = T.ScoreMod(alibi_slopes=sl.to(DEV))
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.empty_like(qg)
+    lse = torch.empty(1, H, N, dtype=torch.float32, device=DEV)
+    T.attn_fwd(qg, kg, vg, o, lse, 0.125, T.Mask(causal=True), smod=sg)
+    torch.cuda.synchronize()
+    p = np.arange(N)
+    for h in range(H):
+        a = float(sl[h])
+        want = np.log((1 - np.exp(-a * (p + 1))) / (1 - np.exp(-a)))
+        err = np.max(np.abs(lse[0, h].cpu().numpy() - want))
+        assert err < 2e-5, (h, err)
+
+
+DECODE = [
+    # (id, B, Hq, Hkv, Lq, Nk, D, seq_lens, S, mask, kind)
+    ("alibi_causal", 2, 8, 2, 5, 300, 128, [300, 171], 3, None, "alibi"),
+    ("alibi_sym_window", 2, 4, 2, 8, 3000, 128, [3000, 2500], 4, (2048, 2048), "alibi_sym"),
+    ("alibi_d64_gqa8", 1, 8, 1, 4, 333, 64, [333], 5, None, "alibi"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_score_mod(case):
+    name, B, Hq, Hkv, Lq, Nk, D, sl, S, win, kind = case
+    announce(f"score_mod decode {name}")
+    pages = (Nk + 15) // 16
+    wl = W.paged_decode("sm" + name, B, Hq, Hkv, Lq, Nk, D, page_size=16, pool_pages=B * pages + 3,
+                        seed=11 + len(name), seq_lens=sl)
+    t = wl.tensors
+    slopes = alibi_slopes(Hq)
+    sg = T.ScoreMod(alibi_slopes=slopes.to(DEV), symmetric="sym" in kind)
+    ws_o = torch.empty(B, Hq, Lq, S, D, dtype=torch.float32, device=DEV)
+    ws_l = torch.empty(B, Hq, Lq, S, dtype=torch.float32, device=DEV)
+    gmask = T.Mask(window=win) if win else None
+    T.attn_decode_splitkv(t["q"].to(DEV), t["k_pool"].to(DEV), t["v_pool"].to(DEV), t["block_table"].to(DEV),
+                          t["seq_lens"].to(DEV), pages, S, ws_o, ws_l, wl.scale, gmask, smod=sg)
+    o = torch.empty(B, Hq, Lq, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=DEV)
+    T.attn_decode_combine(ws_o, ws_l, o, lse)
+    torch.cuda.synchronize()
+    kp, vp, bt = f64(t["k_pool"]), f64(t["v_pool"]), t["block_table"].numpy()
+    for b in range(B):
+        kl = OP.gather(kp, bt, b, sl[b])[None]
+        vl = OP.gather(vp, bt, b, sl[b])[None]
+        mod = M.window(win[0], win[1], Lq, sl[b]) if win else M.causal(Lq, sl[b])
+        smod = (SM.alibi_sym if "sym" in kind else SM.alibi)(slopes.double().numpy(), Lq, sl[b])
+        ro, rl = oracle.attention(f64(t["q"])[b:b + 1], kl, vl, wl.scale, mod, score_mod=smod)
+        assert_close(f64(o[b:b + 1]), f64(lse[b:b + 1]), ro, rl, f"{name} b{b}")
+
+
+BACKWARD = [
+    # (id, B, Hq, Hkv, Nq, Nk, D, mask spec, kind, dtype)
+    ("alibi_causal_d64_gqa", 1, 4, 2, 500, 500, 64, {"causal": True}, "alibi", "bf16"),
+    ("rel_causal_d128", 1, 2, 1, 400, 400, 128, {"causal": True}, "rel", "bf16"),
+    ("alibi_sym_window_d64", 1, 2, 2, 600, 600, 64, {"window": (50, 50)}, "alibi_sym+rel", "bf16"),
+    ("alibi_causal_d128_fp16", 1, 2, 2, 300, 300, 128, {"causal": True}, "alibi", "fp16"),
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD, ids=[c[0] for c in BACKWARD])
+def test_backward_score_mod(case):
+    name, B, Hq, Hkv, Nq, Nk, D, mspec, kind, dt = case
+    if D == 64:
+        pytest.skip(D64_OFF)
+    announce(f"score_mod backward {name}")
+    dtype = torch.float16 if dt == "fp16" else torch.bfloat16
+    g = W.generator(zlib.crc32(name.encode()) % 9973)
+    q = W.randn_half(g, (B, Hq, Nq, D), dtype)
+    k = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    v = W.randn_half(g, (B, Hkv, Nk, D), dtype)
+    do = W.randn_half(g, (B, Hq, Nq, D), dtype)
+    scale = 1.0 / math.sqrt(D)
+    gm, mod = _mask_pair(mspec, B, Nq, Nk)
+    sg, smod, keep = _smod_pair(kind, Hq, Nq, Nk, R=32, seed=5)
+    qg, kg, vg, dog = (x.to(DEV) for x in (q, k, v, do))
+    o = torch.empty_like(qg)
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=DEV)
+    T.attn_fwd(qg, kg, vg, o, lse, scale, gm, smod=sg)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (qg, kg, vg))
+    T.attn_bwd(qg, kg, vg, o, dog, lse, dq, dk, dv, None, scale, gm, smod=sg)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod, score_mod=smod)
+    assert_close(f64(o), f64(lse), ro, rl, f"{name} forward")
+    rq, rk, rv, (mq, mk, mv) = OBW.attention_bwd(f64(q), f64(k), f64(v), f64(do), scale, mod,
+                                                 row_block=256, bound=True, o_used=f64(o),
+                                                 score_mod=smod)
+    assert_grad_close(f64(dq), rq, mq, f"{name} dQ")
+    assert_grad_close(f64(dk), rk, mk, f"{name} dK")
+    assert_grad_close(f64(dv), rv, mv, f"{name} dV")

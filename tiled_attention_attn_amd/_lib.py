@@ -49,6 +49,20 @@ class attn_mask_desc(ctypes.Structure):
     ]
 
 
+class attn_score_mod(ctypes.Structure):
+    _fields_ = [
+        ("flags", ctypes.c_uint32),
+        ("slopes", ctypes.c_void_p),
+        ("rel_bias", ctypes.c_void_p),
+        ("rel_radius", ctypes.c_int32),
+    ]
+
+
+SCORE_ALIBI = 1
+SCORE_ALIBI_SYM = 2
+SCORE_REL_BIAS = 4
+
+
 class attn_blockmask(ctypes.Structure):
     _fields_ = [
         ("Bm", ctypes.c_int32), ("Hm", ctypes.c_int32),
@@ -67,19 +81,20 @@ def _load():
     I64 = ctypes.c_int64
     STR = ctypes.POINTER(ctypes.c_int64)
     MP = ctypes.POINTER(attn_mask_desc)
+    SP = ctypes.POINTER(attn_score_mod)
     BP = ctypes.POINTER(attn_blockmask)
     sig = {
-        "attn_fwd": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, P]),
-        "attn_fwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, BP, P]),
+        "attn_fwd": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, SP, P]),
+        "attn_fwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, SP, BP, P]),
         "attn_build_blockmask": (I, [MP, P, I, I, I, BP, P]),
         "attn_blockmask_bytes": (S, [I, I, I, I]),
-        "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, I, F, MP, P, P, P]),
+        "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, I, F, MP, SP, P, P, P]),
         "attn_decode_combine": (I, [P, P, I, I, I, I, I, I, P, STR, P, P]),
         "attn_decode_ws_o_bytes": (S, [I, I, I, I, I]),
         "attn_decode_ws_lse_bytes": (S, [I, I, I, I]),
         "attn_decode_num_splits": (I, [I, I, I, I]),
         "attn_bwd": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
-                         I, I, I, I, I, I, I, F, MP, P, S, P]),
+                         I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
         "attn_bwd_workspace_bytes": (S, [I, I, I]),
         "attn_status_str": (ctypes.c_char_p, [I]),
         "attn_abi_version": (I, []),
@@ -180,7 +195,46 @@ def _mask_ptr(mask):
     return d, ctypes.byref(d)
 
 
-def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None):
+@dataclass
+class ScoreMod:
+    """Additive score changes of attn_score_mod (d = key index - query position):
+
+    alibi_slopes: float32 [Hq] on the GPU -> + slope * d (or - slope * |d| with
+    symmetric=True);  rel_bias: float32 [Hq, 2R+1] on the GPU -> + rel_bias[h][clamp(d, -R, R) + R].
+    """
+    alibi_slopes: torch.Tensor | None = None
+    symmetric: bool = False
+    rel_bias: torch.Tensor | None = None
+
+    def desc(self) -> attn_score_mod:
+        d = attn_score_mod()
+        d.flags = 0
+        d.slopes = d.rel_bias = None
+        d.rel_radius = 0
+        if self.alibi_slopes is not None:
+            t = self.alibi_slopes
+            if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+                raise TypeError("alibi_slopes must be a contiguous float32 [Hq] tensor")
+            d.flags |= SCORE_ALIBI_SYM if self.symmetric else SCORE_ALIBI
+            d.slopes = t.data_ptr()
+        if self.rel_bias is not None:
+            t = self.rel_bias
+            if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous() or t.shape[1] % 2 != 1:
+                raise TypeError("rel_bias must be a contiguous float32 [Hq, 2R+1] tensor")
+            d.flags |= SCORE_REL_BIAS
+            d.rel_bias = t.data_ptr()
+            d.rel_radius = (t.shape[1] - 1) // 2
+        return d
+
+
+def _smod_ptr(smod):
+    if smod is None:
+        return None, None
+    d = smod.desc() if isinstance(smod, ScoreMod) else smod
+    return d, ctypes.byref(d)
+
+
+def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None, smod=None):
     """O (and LSE) for q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] bf16 or fp16 CUDA tensors (any B/H/N
     strides)."""
     dt = _half(q, k, v, o)
@@ -188,8 +242,9 @@ def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None):
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
     st = _lib.attn_fwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-                       _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale, mp,
+                       _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, sp,
                        _stream(stream))
     _check("attn_fwd", st)
     return o, lse
@@ -231,16 +286,18 @@ def attn_build_blockmask(bm: BlockMask, B, Nq, Nk, mask=None, tile_map=None, str
     return bm
 
 
-def attn_fwd_blockmask(q, k, v, o, bm: BlockMask, lse=None, scale=None, mask=None, stream=None):
+def attn_fwd_blockmask(q, k, v, o, bm: BlockMask, lse=None, scale=None, mask=None, stream=None,
+                       smod=None):
     dt = _half(q, k, v, o)
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
     s = bm.struct()
     st = _lib.attn_fwd_blockmask(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                  _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale,
-                                 mp, ctypes.byref(s), _stream(stream))
+                                 mp, sp, ctypes.byref(s), _stream(stream))
     _check("attn_fwd_blockmask", st)
     return o, lse
 
@@ -260,7 +317,7 @@ def attn_decode_ws_lse_bytes(B, Hq, Lq, S):
 
 
 def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, num_splits,
-                        ws_o, ws_lse, scale=None, mask=None, stream=None):
+                        ws_o, ws_lse, scale=None, mask=None, stream=None, smod=None):
     """Split-KV partials: q [B,Hq,Lq,D]; caches [pages, page_size, Hkv, D] (contiguous);
     block_table int32 [B, >=max_pages]; seq_lens int32 [B]; ws_o float [B,Hq,Lq,S,D];
     ws_lse float [B,Hq,Lq,S]."""
@@ -286,10 +343,11 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, n
         raise ValueError("workspace too small")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
     st = _lib.attn_decode_splitkv(_ptr(q), _strides(q), _ptr(k_cache), _ptr(v_cache), n_pages,
                                   _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
                                   int(max_pages), B, Hq, Hkv, Lq, D, dt, page_size, int(num_splits),
-                                  scale, mp, _ptr(ws_o), _ptr(ws_lse), _stream(stream))
+                                  scale, mp, sp, _ptr(ws_o), _ptr(ws_lse), _stream(stream))
     _check("attn_decode_splitkv", st)
     return ws_o, ws_lse
 
@@ -310,7 +368,8 @@ def attn_bwd_workspace_bytes(B, Hq, Nq):
     return int(_lib.attn_bwd_workspace_bytes(B, Hq, Nq))
 
 
-def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=None, stream=None):
+def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=None, stream=None,
+             smod=None):
     """dQ, dK, dV (written into dq / dk / dv) for q/o/d_o [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] (bf16 or fp16)
     and the forward pass's lse float [B,Hq,Nq]; ``workspace`` is a float32 CUDA tensor of at
     least attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here if None)."""
@@ -326,10 +385,11 @@ def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=
         raise TypeError("workspace must be contiguous float32")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
     st = _lib.attn_bwd(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                        _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse),
                        _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
-                       B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, _ptr(workspace), workspace.numel() * 4,
+                       B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, sp, _ptr(workspace), workspace.numel() * 4,
                        _stream(stream))
     _check("attn_bwd", st)
     return dq, dk, dv

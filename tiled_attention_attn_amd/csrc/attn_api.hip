@@ -65,6 +65,33 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
   return ATTN_OK;
 }
 
+// Converts the public score_mod descriptor.  `allow_rel` is false for
+// decode; `G_bwd` > 0 (the backward pass) also bounds the G tables one
+// work group stages.  `prefill_d64`: the prefill and backward kernels at
+// D = 64 are not offered with a score change (their score-change variants
+// are switched off after a GPU memory fault whose cause is not yet found).
+int make_smod(const attn_score_mod* m, bool allow_rel, int G_bwd, bool prefill_d64,
+              ScoreParams& out) {
+  out = ScoreParams{0u, nullptr, nullptr, 0};
+  if (m == nullptr || m->flags == 0) return ATTN_OK;
+  const uint32_t f = m->flags;
+  if (prefill_d64) return ATTN_ERR_SCORE_MOD;
+  if (f & ~ATTN_SCORE_ALL) return ATTN_ERR_SCORE_MOD;
+  if ((f & ATTN_SCORE_ALIBI) && (f & ATTN_SCORE_ALIBI_SYM)) return ATTN_ERR_SCORE_MOD;
+  if ((f & (ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM)) && m->slopes == nullptr) return ATTN_ERR_NULL;
+  if (f & ATTN_SCORE_REL_BIAS) {
+    if (!allow_rel) return ATTN_ERR_SCORE_MOD;
+    if (m->rel_bias == nullptr) return ATTN_ERR_NULL;
+    if (m->rel_radius < 0 || 2 * m->rel_radius + 1 > kMaxRelTable) return ATTN_ERR_SCORE_MOD;
+    if (G_bwd > 0 && (int64_t)G_bwd * (2 * m->rel_radius + 1) > 8192) return ATTN_ERR_SCORE_MOD;
+  }
+  out.flags = f;
+  out.slopes = m->slopes;
+  out.rel = m->rel_bias;
+  out.R = m->rel_radius;
+  return ATTN_OK;
+}
+
 int check_common(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
                  const void* v, const int64_t* vs, const void* o, const int64_t* os, int B,
                  int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale) {
@@ -123,7 +150,7 @@ void set_slots(FwdParams& p, bool paired) {
 
 extern "C" {
 
-int attn_abi_version(void) { return 3; }
+int attn_abi_version(void) { return 4; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -140,6 +167,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_BLOCKMASK: return "BlockMask descriptor inconsistent with the shapes";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_DTYPE: return "dtype must be ATTN_DTYPE_BF16 or ATTN_DTYPE_F16";
+    case ATTN_ERR_SCORE_MOD: return "bad score_mod flags or parameters, or a score_mod this entry point does not take";
     default: return "unknown status";
   }
 }
@@ -147,12 +175,13 @@ const char* attn_status_str(int status) {
 int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
              const void* v, const int64_t v_stride[3], void* o, const int64_t o_stride[3],
              float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
-             const attn_mask_desc* mask, hipStream_t stream) {
+             const attn_mask_desc* mask, const attn_score_mod* smod, hipStream_t stream) {
   int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
                         D, dtype, scale);
   if (st) return st;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_smod(smod, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
@@ -195,7 +224,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
                        const int64_t k_stride[3], const void* v, const int64_t v_stride[3],
                        void* o, const int64_t o_stride[3], float* lse, int B, int Hq, int Hkv,
                        int Nq, int Nk, int D, int dtype, float scale, const attn_mask_desc* mask,
-                       const attn_blockmask* bm, hipStream_t stream) {
+                       const attn_score_mod* smod, const attn_blockmask* bm, hipStream_t stream) {
   int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
                         D, dtype, scale);
   if (st) return st;
@@ -205,6 +234,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_smod(smod, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   p.part_num = bm->part_num; p.part_idx = bm->part_idx;
@@ -244,8 +274,8 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
                         const void* v_cache, int64_t num_pages, const int32_t* block_table,
                         int64_t bt_stride, const int32_t* seq_lens, int max_pages, int B, int Hq,
                         int Hkv, int Lq, int D, int dtype, int page_size, int num_splits, float scale,
-                        const attn_mask_desc* mask, float* ws_o, float* ws_lse,
-                        hipStream_t stream) {
+                        const attn_mask_desc* mask, const attn_score_mod* smod, float* ws_o,
+                        float* ws_lse, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !ws_o || !ws_lse)
     return ATTN_ERR_NULL;
   int st = check_strides(q_stride);
@@ -267,6 +297,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
+  if ((st = make_smod(smod, false, 0, false, p.smod))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
   p.q = q;
@@ -317,8 +348,8 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
              const void* d_o, const int64_t do_stride[3], const float* lse, void* dq,
              const int64_t dq_stride[3], void* dk, const int64_t dk_stride[3], void* dv,
              const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
-             int dtype, float scale, const attn_mask_desc* mask, float* workspace,
-             size_t workspace_bytes, hipStream_t stream) {
+             int dtype, float scale, const attn_mask_desc* mask, const attn_score_mod* smod,
+             float* workspace, size_t workspace_bytes, hipStream_t stream) {
   // Tensors without rows may be NULL (an empty tensor has no storage).
   if (Nq > 0 && (!q || !o || !d_o || !dq || !lse)) return ATTN_ERR_NULL;
   if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
@@ -344,6 +375,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if ((st = check_scale(scale))) return st;
   BwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_smod(smod, true, Hq / Hkv, D == 64, p.smod))) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   p.q = q;

@@ -108,8 +108,11 @@ __device__ __forceinline__ void key_rows(const MaskParams& m, int b, int key, in
 // Query rows per kv-kernel step: 64 at D=64, 32 at D=128 (a Q or dO tile is
 // 8 KB either way; a stage adds 1 KB for L2 and Delta).
 template <int D> struct BwdQRows { static constexpr int value = D == 64 ? 64 : 32; };
+// Bias-table floats the kv kernel stages for the G query heads of a KV head:
+// G (2R + 1) <= 8192 (the host checks it).
+constexpr int kMaxRelTables = 8192;
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem, int kt, int b,
                                         int kvh) {
   constexpr int QB = BwdQRows<D>::value;
@@ -143,6 +146,15 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       vf[c] = *reinterpret_cast<const vec8<T>*>(vs + 16 * c);
     }
     wait_vmem();
+  }
+
+  // Score change (SM): the G query heads' bias tables in LDS after the ring
+  // (staged before the first copy; the first step's barrier publishes them).
+  TATTN_LDS float* tabs = reinterpret_cast<TATTN_LDS float*>(smem + 2 * STAGE_BYTES);
+  if constexpr (SM) {
+    if (p.smod.flags & ATTN_SCORE_REL_BIAS)
+      for (int g = 0; g < p.G; ++g)
+        stage_rel_table(p.smod, kvh * p.G + g, tabs + g * (2 * p.smod.R + 1), tid, kBwdThreads);
   }
 
   int qa = 0x3fffffff, qb = -1;
@@ -257,14 +269,15 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 #pragma unroll
   for (int d = 0; d < NDB; ++d) dk[d] = dv[d] = f32x16{};
 
-  int qi = 0;
+  int qi = 0, gcur = 0;
   auto step = [&](auto stc, int s) {
     constexpr int ST = decltype(stc)::value;
     wait_vmem();
     lds_barrier();
     if (s + 1 < n_steps) load_next(ST ^ 1);
     const int q0 = qs0 + qi * QB;
-    if (++qi == n_qs) qi = 0;
+    const int g = gcur;
+    if (++qi == n_qs) { qi = 0; ++gcur; }
     if (q0 > w_hi || q0 + QB - 1 < w_lo) return;  // no key of this wave is seen by these rows
     const bool full = w_lo_max <= q0 && w_hi_min >= q0 + QB - 1;
     const TATTN_LDS char* tQ = smem + ST * STAGE_BYTES;
@@ -303,6 +316,13 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
           if (base + off > width) sacc[blk][r] = kNegInf;
         }
     }
+    if constexpr (SM) {
+      // scores now carry c2 and the bias of query head kvh G + g
+      const ScoreHead hd{alibi_slope2(p.smod, kvh * p.G + g), tabs + g * (2 * p.smod.R + 1)};
+      const int d0 = key - (int)(q0 + 4 * half + shift);
+      add_score_bias<NQB, 16>(sacc, p.c2, p.smod, hd,
+                              [&](int blk, int r) { return d0 - (32 * blk + 8 * (r >> 2) + (r & 3)); });
+    }
 #pragma unroll
     for (int blk = 0; blk < NQB; ++blk) {
       const uint32_t roff = blk * 32 * ROW_BYTES;
@@ -316,7 +336,7 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       float pr[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pr[r] = fast_exp2(__builtin_fmaf(sacc[blk][r], p.c2, -l2[r >> 2][r & 3]));
+        pr[r] = fast_exp2(__builtin_fmaf(sacc[blk][r], SM ? 1.f : p.c2, -l2[r >> 2][r & 3]));
         ds[r] = pr[r] * (dpacc[blk][r] - dl[r >> 2][r & 3]);
       }
       vec8<T> pp[2], pd[2];
@@ -370,12 +390,13 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 // 512-entry register file of one SIMD lane.
 template <int D> struct BwdKvOcc { static constexpr int value = D == 64 ? 2 : 1; };
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kBwdThreads)
 __attribute__((amdgpu_waves_per_eu(BwdKvOcc<D>::value, BwdKvOcc<D>::value)))
 bwd_kv_kernel(const BwdParams p) {
   constexpr int STAGE_BYTES = 2 * BwdQRows<D>::value * D * 2 + 1024;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES];
+  // the ring (34 KB), then the G bias tables (up to 32 KB) when SM
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES + (SM ? kMaxRelTables * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.kv_xcd_remap) {
@@ -386,12 +407,12 @@ bwd_kv_kernel(const BwdParams p) {
   const int slot = unit % p.kv_slots;
   const int r = unit / p.kv_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
-  kv_tile<D, T>(p, smem, slot, b, kvh);
+  kv_tile<D, T, SM>(p, smem, slot, b, kvh);
   if (p.kv_paired) {
     const int kt2 = p.n_kt - 1 - slot;
     if (kt2 != slot) {
       __syncthreads();
-      kv_tile<D, T>(p, smem, kt2, b, kvh);
+      kv_tile<D, T, SM>(p, smem, kt2, b, kvh);
     }
   }
 }
@@ -400,7 +421,7 @@ bwd_kv_kernel(const BwdParams p) {
 // Keys per step as in the forward kernel: 128 at D=64, 64 at D=128.
 template <int D> struct BwdKBlk { static constexpr int value = D == 64 ? 128 : 64; };
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem, int qt, int b,
                                        int h, int kvh) {
   constexpr int kKBlk = BwdKBlk<D>::value;
@@ -441,6 +462,14 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
 
   int lo, hi;
   row_interval(p.mask, b, qrow + shift, p.Nk, lo, hi);
+  // Score change (SM): slope and LDS bias table of the head, after the ring.
+  ScoreHead hd{0.f, nullptr};
+  if constexpr (SM) {
+    hd.slope2 = alibi_slope2(p.smod, h);
+    TATTN_LDS float* tab = reinterpret_cast<TATTN_LDS float*>(smem + 2 * STAGE_BYTES);
+    hd.tab = tab;
+    if (p.smod.flags & ATTN_SCORE_REL_BIAS) stage_rel_table(p.smod, h, tab, tid, kBwdThreads);
+  }
   int n_steps = 0, kb_begin = 0, lo_last = 0, hi_first = 0;
   {
     int lo_first, hi_last, t0;
@@ -542,10 +571,15 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
           if (base_ok + off > width) sacc[r] = kNegInf;
         }
       }
+      if constexpr (SM) {
+        const int d0 = kb + 32 * kbk + 4 * half - (int)(qrow + shift);
+        add_score_bias<1, 16>(&sacc, p.c2, p.smod, hd,
+                              [&](int, int r) { return d0 + 8 * (r >> 2) + (r & 3); });
+      }
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        ds[r] = fast_exp2(__builtin_fmaf(sacc[r], p.c2, -l2)) * (dpacc[r] - dl);
+        ds[r] = fast_exp2(__builtin_fmaf(sacc[r], SM ? 1.f : p.c2, -l2)) * (dpacc[r] - dl);
       // ---- dQ^T += K^T dS^T over these 32 keys (two 16-key chunks) ----
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -582,10 +616,12 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
   }
 }
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2];
+  // the ring (64 KB), then the head's bias table (8 KB) when SM
+  __shared__ __attribute__((aligned(1024)))
+  char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.q_xcd_remap) {
@@ -599,12 +635,12 @@ bwd_q_kernel(const BwdParams p) {
   r /= p.q_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  q_tile<D, T>(p, smem, slot, b, h, kvh);
+  q_tile<D, T, SM>(p, smem, slot, b, h, kvh);
   if (p.q_paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      q_tile<D, T>(p, smem, qt2, b, h, kvh);
+      q_tile<D, T, SM>(p, smem, qt2, b, h, kvh);
     }
   }
 }
@@ -612,8 +648,13 @@ bwd_q_kernel(const BwdParams p) {
 template <int D, typename T>
 void launch_bwd_t(const BwdParams& p, dim3 gpre, dim3 gkv, dim3 gq, dim3 block, hipStream_t stream) {
   if (gpre.x) hipLaunchKernelGGL((bwd_pre_kernel<D, T>), gpre, block, 0, stream, p);
-  if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T>), gkv, block, 0, stream, p);
-  if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T>), gq, block, 0, stream, p);
+  if (p.smod.flags) {
+    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, true>), gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, true>), gq, block, 0, stream, p);
+  } else {
+    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, false>), gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, false>), gq, block, 0, stream, p);
+  }
 }
 
 int launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t stream) {

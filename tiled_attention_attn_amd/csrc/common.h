@@ -240,4 +240,72 @@ __device__ __forceinline__ void row_interval(const MaskParams& m, int b, int64_t
   hi_out = (int)hi;
 }
 
+// ---- score_mod ---------------------------------------------------------------
+// Additive changes of the scaled score before the softmax: ALiBi, symmetric
+// ALiBi, and a relative-position bias table (flags of attn_score_mod).  The
+// kernels work in base-2 units, so a score becomes s c2 + log2(e) bias(d)
+// with d = key - query position.
+struct ScoreParams {
+  uint32_t flags;
+  const float* slopes;  // [Hq]
+  const float* rel;     // [Hq][2R+1]
+  int32_t R;
+};
+
+// Largest relative-bias table a kernel stages in LDS for one head (floats).
+constexpr int kMaxRelTable = 2048;
+
+// The query head's score state: its ALiBi slope in base-2 units and its bias
+// table in LDS (already scaled by log2(e)).
+struct ScoreHead {
+  float slope2;
+  const TATTN_LDS float* tab;
+};
+
+// Copies head h's bias table, times log2(e), into LDS (all threads of the
+// work group take part; the caller's next barrier publishes it).
+__device__ __forceinline__ void stage_rel_table(const ScoreParams& sp, int h, TATTN_LDS float* dst,
+                                                int tid, int nthreads) {
+  const int n = 2 * sp.R + 1;
+  const float* src = sp.rel + (int64_t)h * n;
+  for (int i = tid; i < n; i += nthreads) dst[i] = src[i] * kLog2e;
+}
+
+__device__ __forceinline__ float alibi_slope2(const ScoreParams& sp, int h) {
+  return (sp.flags & (ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM)) ? sp.slopes[h] * kLog2e : 0.f;
+}
+
+// acc[i][r] = acc[i][r] * c2 + log2(e) bias(dist(i, r)) over NB accumulators of
+// NE elements; -inf (masked) stays -inf.  One loop per term behind uniform
+// branches, so no per-element branching.
+template <int NB, int NE, typename V, typename DistFn>
+__device__ __forceinline__ void add_score_bias(V* acc, float c2, const ScoreParams& sp,
+                                               const ScoreHead& hd, DistFn dist) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int r = 0; r < NE; ++r) acc[i][r] *= c2;
+  if (sp.flags & ATTN_SCORE_ALIBI) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < NE; ++r) acc[i][r] = __builtin_fmaf(hd.slope2, (float)dist(i, r), acc[i][r]);
+  } else if (sp.flags & ATTN_SCORE_ALIBI_SYM) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < NE; ++r)
+        acc[i][r] = __builtin_fmaf(-hd.slope2, __builtin_fabsf((float)dist(i, r)), acc[i][r]);
+  }
+  if (sp.flags & ATTN_SCORE_REL_BIAS) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < NE; ++r) {
+        const int d = dist(i, r);
+        acc[i][r] += hd.tab[(d < -sp.R ? -sp.R : (d > sp.R ? sp.R : d)) + sp.R];
+      }
+  }
+}
+
 }  // namespace tattn

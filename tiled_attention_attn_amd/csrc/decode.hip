@@ -50,7 +50,7 @@ __device__ __forceinline__ uint32_t dec_tile_off(uint32_t row, uint32_t chunk) {
 
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(const DecParams p) {
   constexpr int kDecKBlk = DecKBlk<D>::value;
@@ -115,6 +115,14 @@ decode_kernel(const DecParams p) {
     wlo = max(wlo, __shfl_xor(wlo, m, 64));
     whi = min(whi, __shfl_xor(whi, m, 64));
   }
+
+  // Score change (SM): ALiBi only here (the host rejects a bias table); the
+  // lane's query head hq sets its slope.  Scores then carry c2 and the bias.
+  ScoreParams sp = p.smod;
+  sp.flags &= ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM;
+  ScoreHead hd{0.f, nullptr};
+  if constexpr (SM) hd.slope2 = alibi_slope2(sp, hq);
+  const float c2e = SM ? 1.f : p.c2;
 
   // Q^T fragments (B operand, k = head dim, n = row).
   vec8<T> qf[NC];
@@ -195,6 +203,11 @@ decode_kernel(const DecParams p) {
           if (key < lo || key > hi) sacc[kb16][r] = kNegInf;
         }
     }
+    if constexpr (SM) {
+      // element (kb16, r) holds key kb + 16 kb16 + 4 grp + r
+      const int d0 = kb + 4 * grp - (int)pos;
+      add_score_bias<NKB, 4>(sacc, p.c2, sp, hd, [&](int kb16, int r) { return d0 + 16 * kb16 + r; });
+    }
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb16 = 0; kb16 < NKB; ++kb16)
@@ -202,7 +215,7 @@ decode_kernel(const DecParams p) {
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb16][r]);
     mx = fmaxf(mx, xor_lane(mx, 16));
     mx = fmaxf(mx, xor_lane(mx, 32));
-    const float m_new = fmaxf(m_run, mx * p.c2);
+    const float m_new = fmaxf(m_run, mx * c2e);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
@@ -215,7 +228,7 @@ decode_kernel(const DecParams p) {
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(__builtin_fmaf(sacc[2 * kc + (i >> 2)][i & 3], p.c2, -m_use));
+        e[i] = fast_exp2(__builtin_fmaf(sacc[2 * kc + (i >> 2)][i & 3], c2e, -m_use));
         l_run += e[i];
       }
       pf[kc] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
@@ -299,16 +312,22 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m_use + logf(tot) : kNegInf;
 }
 
-template <typename T>
+template <typename T, bool SM>
 void launch_decode_t(const DecParams& p, int D, dim3 grid, dim3 block, hipStream_t stream) {
-  if (D == 64) hipLaunchKernelGGL((decode_kernel<64, T>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((decode_kernel<128, T>), grid, block, 0, stream, p);
+  if (D == 64) hipLaunchKernelGGL((decode_kernel<64, T, SM>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel<128, T, SM>), grid, block, 0, stream, p);
 }
 
 int launch_decode(const DecParams& p, int D, int dtype, hipStream_t stream) {
   dim3 grid(p.S * p.n_rg, p.Hkv, p.B), block(kDecThreads);
-  if (dtype == ATTN_DTYPE_F16) launch_decode_t<f16>(p, D, grid, block, stream);
-  else launch_decode_t<bf16>(p, D, grid, block, stream);
+  const bool sm = p.smod.flags != 0;
+  if (dtype == ATTN_DTYPE_F16) {
+    if (sm) launch_decode_t<f16, true>(p, D, grid, block, stream);
+    else launch_decode_t<f16, false>(p, D, grid, block, stream);
+  } else {
+    if (sm) launch_decode_t<bf16, true>(p, D, grid, block, stream);
+    else launch_decode_t<bf16, false>(p, D, grid, block, stream);
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -53,7 +53,7 @@ struct Step {
   int use_row_interval;  // 1: the row's own mask interval; 0: only k < Nk
 };
 
-template <int D, bool BM, int NST, typename T>
+template <int D, bool BM, int NST, typename T, bool SM>
 __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char* smem, int qt,
                                              int b, int h, int kvh) {
   constexpr int kKBlk = KBlk<D>::value;
@@ -95,6 +95,19 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
 
   int lo, hi;
   row_interval(p.mask, b, qrow + shift, p.Nk, lo, hi);
+
+  // Score change (SM): the head's ALiBi slope and bias table, staged in LDS
+  // after the ring before the first copy (the first step's barrier
+  // publishes it).  Scores then carry c2 and the bias, so the softmax below
+  // runs with unit scale.
+  ScoreHead hd{0.f, nullptr};
+  if constexpr (SM) {
+    hd.slope2 = alibi_slope2(p.smod, h);
+    TATTN_LDS float* tab = reinterpret_cast<TATTN_LDS float*>(smem + NST * STAGE_BYTES);
+    hd.tab = tab;
+    if (p.smod.flags & ATTN_SCORE_REL_BIAS) stage_rel_table(p.smod, h, tab, tid, kThreads);
+  }
+  const float c2e = SM ? 1.f : p.c2;
 
   // Step list.
   int n_steps = 0, kb_begin = 0, lo_last = 0, hi_first = 0;
@@ -248,6 +261,11 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
           if (base_ok + off > width) sacc[kbk][r] = kNegInf;
         }
     }
+    if constexpr (SM) {
+      const int d0 = st.kb + 4 * half - (int)(qrow + shift);
+      add_score_bias<NKB, 16>(sacc, p.c2, p.smod, hd,
+                              [&](int kbk, int r) { return d0 + 32 * kbk + 8 * (r >> 2) + (r & 3); });
+    }
     // ---- online softmax against a lazily moved reference max ----
     // P = exp2(c2 s - m_ref) is taken against the row's reference m_ref
     // without a row max on the common path.  Every P value of a lane is at
@@ -266,7 +284,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
         float e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
+          e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], c2e, -m_use));
           // l sums the fp32 values: summing the rounded P instead would
           // put up to 2^-9 of relative error into LSE.
           if (i & 1) ps1 += e[i]; else ps0 += e[i];
@@ -282,7 +300,7 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
-      mx = fmaxf(mx, other_half(mx)) * p.c2;
+      mx = fmaxf(mx, other_half(mx)) * c2e;
       const float m_new = fmaxf(m_ref, mx);
       // A row that has seen no key yet has O = 0 and l = 0: alpha must be 0
       // there, also when its m_new is still -inf (exp2(-inf - -inf) is NaN).
@@ -341,11 +359,13 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
 // per wave each).
 template <int D> struct Occ { static constexpr int value = 2; };
 
-template <int D, bool BM, typename T>
+template <int D, bool BM, typename T, bool SM>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Occ<D>::value, Occ<D>::value)))
 fwd_kernel(const FwdParams p) {
   constexpr int NST = Stages<D>::value;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * KBlk<D>::value * D * 2];
+  // the ring (64 KB), then the score-change table (8 KB) when SM
+  __shared__ __attribute__((aligned(1024)))
+  char smem_raw[NST * 2 * KBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.xcd_remap) {
@@ -363,27 +383,27 @@ fwd_kernel(const FwdParams p) {
   r /= p.n_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  process_tile<D, BM, NST, T>(p, smem, slot, b, h, kvh);
+  process_tile<D, BM, NST, T, SM>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      process_tile<D, BM, NST, T>(p, smem, qt2, b, h, kvh);
+      process_tile<D, BM, NST, T, SM>(p, smem, qt2, b, h, kvh);
     }
   }
 }
 
 int launch_fwd_pp(const FwdParams& p, int D, int dtype, hipStream_t stream);
 
-template <typename T>
+template <typename T, bool SM>
 void launch_fwd_t(const FwdParams& p, int D, bool blockmask, dim3 grid, dim3 block,
                   hipStream_t stream) {
   if (D == 64) {
-    if (blockmask) hipLaunchKernelGGL((fwd_kernel<64, true, T>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_kernel<64, false, T>), grid, block, 0, stream, p);
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<64, true, T, SM>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<64, false, T, SM>), grid, block, 0, stream, p);
   } else {
-    if (blockmask) hipLaunchKernelGGL((fwd_kernel<128, true, T>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((fwd_kernel<128, false, T>), grid, block, 0, stream, p);
+    if (blockmask) hipLaunchKernelGGL((fwd_kernel<128, true, T, SM>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_kernel<128, false, T, SM>), grid, block, 0, stream, p);
   }
 }
 
@@ -393,8 +413,14 @@ int launch_fwd(const FwdParams& p, int D, bool blockmask, int dtype, hipStream_t
   if (!blockmask && D == 128) return launch_fwd_pp(p, D, dtype, stream);
   const long units = (long)p.B * p.Hq * p.n_slots;
   dim3 grid((unsigned)units), block(kThreads);
-  if (dtype == ATTN_DTYPE_F16) launch_fwd_t<f16>(p, D, blockmask, grid, block, stream);
-  else launch_fwd_t<bf16>(p, D, blockmask, grid, block, stream);
+  const bool sm = p.smod.flags != 0;
+  if (dtype == ATTN_DTYPE_F16) {
+    if (sm) launch_fwd_t<f16, true>(p, D, blockmask, grid, block, stream);
+    else launch_fwd_t<f16, false>(p, D, blockmask, grid, block, stream);
+  } else {
+    if (sm) launch_fwd_t<bf16, true>(p, D, blockmask, grid, block, stream);
+    else launch_fwd_t<bf16, false>(p, D, blockmask, grid, block, stream);
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

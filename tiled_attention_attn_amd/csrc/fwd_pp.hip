@@ -40,7 +40,7 @@ template <int D> struct PPKBlk { static constexpr int value = D == 64 ? 128 : 64
 // A lane's partial row sum of P above 2^12 moves the reference max.
 constexpr float kPPSumCap = 4096.0f;
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem, int qt, int b,
                                         int h, int kvh) {
   constexpr int KB = PPKBlk<D>::value;
@@ -80,6 +80,17 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   }
   int lo, hi;
   row_interval(p.mask, b, qrow + shift, p.Nk, lo, hi);
+
+  // Score change (SM): slope and LDS bias table of the head, staged after
+  // the ring before the first copy; scores then carry c2 and the bias.
+  ScoreHead hd{0.f, nullptr};
+  if constexpr (SM) {
+    hd.slope2 = alibi_slope2(p.smod, h);
+    TATTN_LDS float* tab = reinterpret_cast<TATTN_LDS float*>(smem + kPPStages * STAGE_BYTES);
+    hd.tab = tab;
+    if (p.smod.flags & ATTN_SCORE_REL_BIAS) stage_rel_table(p.smod, h, tab, tid, kPPThreads);
+  }
+  const float c2e = SM ? 1.f : p.c2;
 
   // Steps of the tile: the keys any of its rows sees (interval ends never
   // decrease with the row, so the first and last rows bound them).
@@ -215,7 +226,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], p.c2, -m_use));
+        e[i] = fast_exp2(__builtin_fmaf(sacc[kc >> 1][8 * (kc & 1) + i], c2e, -m_use));
         if (i & 1) ps1 += e[i]; else ps0 += e[i];
       }
       pf[kc] = pack8<T>(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
@@ -241,6 +252,11 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
           if (base_ok + off > width) sacc[kbk][r] = kNegInf;
         }
     }
+    if constexpr (SM) {
+      const int d0 = kb + 4 * half - (int)(qrow + shift);
+      add_score_bias<NKB, 16>(sacc, p.c2, p.smod, hd,
+                              [&](int kbk, int r) { return d0 + 32 * kbk + 8 * (r >> 2) + (r & 3); });
+    }
     // P against the row's reference; the reference moves (O and l rescaled)
     // only when a partial sum shows it stale or the row's first key arrives.
     float psum = probs(m_ref == kNegInf ? 0.f : m_ref);
@@ -250,7 +266,7 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
       for (int kbk = 0; kbk < NKB; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kbk][r]);
-      mx = fmaxf(mx, other_half(mx)) * p.c2;
+      mx = fmaxf(mx, other_half(mx)) * c2e;
       const float m_new = fmaxf(m_ref, mx);
       // A row that has seen no key yet has O = 0 and l = 0: alpha is 0 there.
       const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - m_new);
@@ -322,10 +338,12 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
   }
 }
 
-template <int D, typename T>
+template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pp_kernel(const FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kPPStages * 2 * PPKBlk<D>::value * D * 2];
+  // the ring (64 KB), then the score-change table (8 KB) when SM
+  __shared__ __attribute__((aligned(1024)))
+  char smem_raw[kPPStages * 2 * PPKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   int unit = blockIdx.x;
   if (p.xcd_remap) {
@@ -342,12 +360,12 @@ fwd_pp_kernel(const FwdParams p) {
   r /= p.n_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  pp_tile<D, T>(p, smem, slot, b, h, kvh);
+  pp_tile<D, T, SM>(p, smem, slot, b, h, kvh);
   if (p.paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      pp_tile<D, T>(p, smem, qt2, b, h, kvh);
+      pp_tile<D, T, SM>(p, smem, qt2, b, h, kvh);
     }
   }
 }
@@ -365,8 +383,14 @@ int launch_fwd_pp(const FwdParams& p_in, int D, int dtype, hipStream_t stream) {
   p.xcd_remap = (units % 8) == 0;
   dim3 grid((unsigned)units), block(kPPThreads);
   if (D != 128) return ATTN_ERR_HEAD_DIM;  // D=64 prefill runs on fwd_kernel
-  if (dtype == ATTN_DTYPE_F16) hipLaunchKernelGGL((fwd_pp_kernel<128, f16>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((fwd_pp_kernel<128, bf16>), grid, block, 0, stream, p);
+  const bool sm = p.smod.flags != 0;
+  if (dtype == ATTN_DTYPE_F16) {
+    if (sm) hipLaunchKernelGGL((fwd_pp_kernel<128, f16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_pp_kernel<128, f16, false>), grid, block, 0, stream, p);
+  } else {
+    if (sm) hipLaunchKernelGGL((fwd_pp_kernel<128, bf16, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((fwd_pp_kernel<128, bf16, false>), grid, block, 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -19,6 +19,7 @@ struct FwdParams {
   int B, Hq, Hkv, G, Nq, Nk;
   float c2;  // scale * log2(e): scores live in base-2 units inside the kernel
   MaskParams mask;
+  ScoreParams smod;
   const int32_t* part_num;
   const int32_t* part_idx;
   const int32_t* full_num;
@@ -58,6 +59,7 @@ struct DecParams {
   int64_t num_pages;                    // pool size (page indices are clamped to it)
   float c2;
   MaskParams mask;
+  ScoreParams smod;
   float* ws_o;
   float* ws_lse;
 };
@@ -80,6 +82,7 @@ struct BwdParams {
   float c2;    // scale * log2(e)
   float scale;
   MaskParams mask;
+  ScoreParams smod;
   float* ws_l2;     // [B*Hq][nq_pad]: LSE * log2(e); +inf for empty rows and padding
   float* ws_delta;  // [B*Hq][nq_pad]: rowsum(dO * O); 0 for padding
   int n_kt, kv_slots, kv_paired, kv_xcd_remap;  // 128-key tiles (dK / dV kernel)
