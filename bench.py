@@ -9,7 +9,9 @@ times, each on its own seeded synthetic inputs with inputs resident in HBM:
 
 * decode: split-KV paged decode B=16 Hq=32 Hkv=8, 16 queries over 32768 keys,
   D=128, 16-token pages (splitkv + combine), KV-read GB/s = B*Hkv*Nk*D*2 bytes
-  * 2 (K and V) / time, as a fraction of the 8 TB/s HBM peak;
+  * 2 (K and V) / time, as a fraction of the 8 TB/s HBM peak; and the same
+  keys in contiguous K/V through attn_fwd_auto (split-KV chosen by shape)
+  against attn_fwd's prefill kernels on that call;
 * the other prefill workloads (window+document and block-diffusion at
   B=1 H=32 N=8192 D=128, block-sparse GQA at N=32768), in TFLOP/s;
 * the backward pass (attn_bwd: dQ, dK, dV) on the causal headline shape and
@@ -195,8 +197,22 @@ def bench_decode(T, W, steps, warmup):
     c_avg, _, _ = time_launches(comb, steps, warmup)
     avg, best, wall = time_launches(both, steps, warmup)
     kv_bytes = float(B * Hkv * Nk * D * 2 * 2)
+    # The same keys gathered into contiguous [B, Hkv, Nk, D] K/V: attn_fwd_auto (split-KV +
+    # combine, chosen by shape) against attn_fwd (the prefill kernels) on that call.
+    j = torch.arange(Nk, device="cuda")
+    page, slot = bt[:, j // 16].long(), (j % 16)[None]
+    kc = kp[page, slot].permute(0, 2, 1, 3).contiguous()
+    vc = vp[page, slot].permute(0, 2, 1, 3).contiguous()
+    del kp, vp, page
+    plan = T.attn_fwd_auto_plan(B, Hq, Hkv, Lq, Nk, D)
+    ws = torch.empty(plan.workspace_bytes // 4, dtype=torch.float32, device="cuda")
+    cm = T.Mask(causal=True).desc()
+    a_avg, a_min, _ = time_launches(lambda: T.attn_fwd_auto(q, kc, vc, o, lse, scale, cm, ws), steps,
+                                    warmup)
+    p_avg, _, _ = time_launches(lambda: T.attn_fwd(q, kc, vc, o, lse, scale, cm), steps, warmup)
     return dict(avg_ms=avg, min_ms=best, wall_ms=wall, splitkv_ms=s_avg, splitkv_min_ms=s_min,
-                combine_ms=c_avg, splits=S, kv_bytes=kv_bytes)
+                combine_ms=c_avg, splits=S, kv_bytes=kv_bytes, auto_ms=a_avg, auto_min_ms=a_min,
+                auto_path=int(plan.path), auto_splits=int(plan.num_splits), auto_prefill_ms=p_avg)
 
 
 def bench_backward(T, W, steps, warmup):
@@ -306,6 +322,8 @@ def main():
         dec = bench_decode(T, W, args.steps, args.warmup)
         log(f"decode: {dec['avg_ms']*1e3:.1f} us (splitkv {dec['splitkv_ms']*1e3:.1f} + combine "
             f"{dec['combine_ms']*1e3:.1f}), {dec['kv_bytes'] / dec['avg_ms'] / 1e6:.0f} GB/s")
+        log(f"auto (contiguous K/V): {dec['auto_ms']*1e3:.1f} us on path {dec['auto_path']}, "
+            f"prefill kernels {dec['auto_prefill_ms']*1e3:.1f} us")
         return
 
     if args.only == "backward":
@@ -334,7 +352,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd_kernel<64,false>/causal_b2h16n4096d64"),
-                     "traffic_unit": "bytes/launch", "kernel": "fwd_kernel<64, false, __bf16>",
+                     "traffic_unit": "bytes/launch", "kernel": "fwd_kernel<64, false, bf16, false>",
                      "kernel_us": round(pf["avg_ms"] * 1e3, 2)},
     }
     if not args.quick and args.only == "all":
@@ -352,7 +370,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(s_gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(s_gbs / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("decode_kernel<128>/decode_b16h32kv8q16k32768d128"),
-                         "traffic_unit": "bytes/launch", "kernel": "decode_kernel<128, __bf16>"},
+                         "traffic_unit": "bytes/launch",
+                         "kernel": "decode_kernel<128, bf16, false, true>"},
+            "auto_contiguous": {
+                "what": "attn_fwd_auto on the same keys in contiguous [B, Hkv, Nk, D] K/V "
+                        "(split-KV + combine, chosen by shape) vs attn_fwd (prefill kernels)",
+                "path": "splitkv" if dec["auto_path"] == 1 else "prefill",
+                "num_splits": dec["auto_splits"], "us": round(dec["auto_ms"] * 1e3, 2),
+                "min_us": round(dec["auto_min_ms"] * 1e3, 2),
+                "GB/s": round(dec["kv_bytes"] / dec["auto_ms"] / 1e6, 1),
+                "prefill_kernels_us": round(dec["auto_prefill_ms"] * 1e3, 2),
+                "speedup": round(dec["auto_prefill_ms"] / dec["auto_ms"], 2)},
         }
     if not args.quick:
         others = bench_prefill_others(T, W, args.steps, args.warmup)

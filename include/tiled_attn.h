@@ -261,6 +261,51 @@ size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits);
  * groups for every compute unit, never more splits than pages. */
 int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
 
+/* ---- shape-based dispatch ----------------------------------------------------
+ * The FlexAttention article (section 1) describes a decode backend that
+ * notices the "short query, long KV" shape and switches to a FlashDecoding-
+ * style split-KV kernel.  attn_fwd_auto is attn_fwd with that choice made by
+ * shape: same tensors, strides, mask, score_mod and results (O, LSE) as
+ * attn_fwd, on contiguous (non-paged) K/V.
+ *
+ * The split-KV path is taken when all G * Nq query rows of a KV head fit one
+ * 64-row group (G = Hq / Hkv, so G * Nq <= 64), Nk >= 512, and smod carries
+ * no ATTN_SCORE_REL_BIAS.  It runs the split-KV kernel over K/V in place and
+ * then the combine: K/V are read once per KV head rather than once per query
+ * head, and the key splits fill the GPU.  Every other shape runs attn_fwd.
+ *
+ * attn_fwd_auto_plan: the path (ATTN_PATH_*), the key split count and the
+ * workspace bytes attn_fwd_auto needs for a shape; host only, launches
+ * nothing.  Size errors as attn_fwd; ATTN_ERR_NULL when out is NULL.
+ *
+ * attn_fwd_auto: `workspace` is device memory of at least
+ * plan.workspace_bytes, 16-byte aligned, overwritten (fp32 partial O and LSE
+ * of every split); it may be NULL when that is 0.  ATTN_ERR_WORKSPACE when
+ * workspace_bytes is smaller.  On the split-KV path the mask menu is
+ * attn_fwd's (DOCUMENT included) and smod may carry ALiBi at D = 64 and 128;
+ * on the prefill path every attn_fwd rule holds.  Results match attn_fwd to
+ * rounding (a different order of the key sums), not bit for bit.
+ */
+#define ATTN_PATH_PREFILL 0
+#define ATTN_PATH_SPLITKV 1
+
+typedef struct attn_auto_plan {
+  int32_t path;             /* ATTN_PATH_PREFILL or ATTN_PATH_SPLITKV       */
+  int32_t num_splits;       /* key splits of the split-KV path, else 0      */
+  uint64_t workspace_bytes; /* bytes attn_fwd_auto needs, 0 on the prefill path */
+} attn_auto_plan;
+
+int attn_fwd_auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                       const attn_score_mod* smod, attn_auto_plan* out);
+
+int attn_fwd_auto(const void* q, const int64_t q_stride[3],
+                  const void* k, const int64_t k_stride[3],
+                  const void* v, const int64_t v_stride[3],
+                  void* o, const int64_t o_stride[3], float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
+                  const attn_mask_desc* mask, const attn_score_mod* smod,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- backward pass ---------------------------------------------------------
  * Gradients of attn_fwd's O for an upstream gradient dO, by recomputation:
  * only Q, K, V, O and the forward pass's LSE are read, and P is rebuilt tile

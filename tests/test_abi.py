@@ -184,6 +184,70 @@ def test_bwd_argument_errors(T):
                dk=None, dv=None) == 0
 
 
+def test_auto_plan_rule(T):
+    """attn_fwd_auto's choice: split-KV for G * Nq <= 64 rows per KV head and Nk >= 512
+    (no relative-bias table); the split count targets 512 work groups with >= 256 keys each,
+    in whole 64-key steps; workspace = fp32 partial O (padded to 256 B) + partial LSE."""
+    P = T.attn_fwd_auto_plan
+    pl = P(16, 32, 8, 16, 32768, 128)
+    assert (pl.path, pl.num_splits) == (T.PATH_SPLITKV, 4)
+    parts = 16 * 32 * 16 * 4
+    assert pl.workspace_bytes == parts * 128 * 4 + parts * 4
+    assert P(1, 32, 8, 16, 32768, 128).num_splits == 64      # 8 units: 64 splits of 512 keys
+    assert P(1, 1, 1, 1, 1000, 64).num_splits == 3           # <= Nk / 256 splits, chunks of 384
+    assert P(128, 32, 8, 1, 4096, 128).num_splits == 1       # 1024 units already fill the GPU
+    assert P(1, 8, 8, 1, 512, 64).path == T.PATH_SPLITKV
+    assert P(1, 8, 8, 1, 511, 64).path == T.PATH_PREFILL     # too few keys
+    assert P(16, 32, 8, 17, 32768, 128).path == T.PATH_PREFILL  # 68 rows per KV head
+    assert P(1, 64, 1, 1, 32768, 128).path == T.PATH_SPLITKV    # G = 64, one row each
+    assert P(2, 16, 16, 4096, 4096, 64).path == T.PATH_PREFILL
+    assert P(1, 8, 8, 0, 4096, 64).path == T.PATH_PREFILL
+    rel = T.attn_score_mod(flags=T.SCORE_REL_BIAS, rel_bias=16, rel_radius=4)
+    assert P(16, 32, 8, 16, 32768, 128, rel).path == T.PATH_PREFILL
+    ali = T.attn_score_mod(flags=T.SCORE_ALIBI, slopes=16)
+    assert P(16, 32, 8, 16, 32768, 128, ali).path == T.PATH_SPLITKV
+    for B, Hq, Hkv, Nq, Nk in [(3, 12, 4, 5, 700), (1, 2, 1, 32, 99999), (7, 8, 2, 16, 4097)]:
+        pl = P(B, Hq, Hkv, Nq, Nk, 64)
+        assert pl.path == T.PATH_SPLITKV
+        chunk = (-(-Nk // pl.num_splits) + 63) // 64 * 64
+        assert -(-Nk // chunk) == pl.num_splits and (pl.num_splits - 1) * chunk < Nk
+    lib = T.lib_handle()
+    assert lib.attn_fwd_auto_plan(1, 4, 3, 1, 1, 64, None, ctypes.byref(T.attn_auto_plan())) == -4
+    assert lib.attn_fwd_auto_plan(1, 4, 4, 1, 1, 96, None, ctypes.byref(T.attn_auto_plan())) == -3
+    assert lib.attn_fwd_auto_plan(-1, 4, 4, 1, 1, 64, None, ctypes.byref(T.attn_auto_plan())) == -2
+    assert lib.attn_fwd_auto_plan(1, 4, 4, 1, 1, 64, None, None) == -1
+
+
+def test_auto_argument_errors(T):
+    lib = T.lib_handle()
+    qs = _strides(32 * 16 * 128, 16 * 128, 128)
+    ks = _strides(8 * 4096 * 128, 4096 * 128, 128)
+    need = T.attn_fwd_auto_plan(2, 32, 8, 16, 4096, 128).workspace_bytes
+
+    def auto(**kw):
+        a = dict(q=16, k=32, v=48, o=64, lse=None, B=2, Hq=32, Hkv=8, Nq=16, Nk=4096, D=128, dt=0,
+                 scale=0.1, mask=None, smod=None, ws=80, wsb=need)
+        a.update(kw)
+        mk = None if a["mask"] is None else ctypes.byref(a["mask"])
+        sm = None if a["smod"] is None else ctypes.byref(a["smod"])
+        return lib.attn_fwd_auto(a["q"], qs, a["k"], ks, a["v"], ks, a["o"], qs, a["lse"], a["B"], a["Hq"],
+                                 a["Hkv"], a["Nq"], a["Nk"], a["D"], a["dt"], a["scale"], mk, sm, a["ws"],
+                                 a["wsb"], None)
+    assert auto(ws=None) == -1
+    assert auto(wsb=need - 1) == -8
+    assert auto(ws=88) == -6
+    assert auto(k=None) == -1
+    assert auto(D=80) == -3
+    assert auto(dt=4) == -12
+    assert auto(Hkv=5) == -4
+    assert auto(scale=float("nan")) == -11
+    assert auto(mask=T.attn_mask_desc(flags=64)) == -7
+    assert auto(smod=T.attn_score_mod(flags=1, slopes=None)) == -1
+    # the prefill path keeps attn_fwd's rules: no score change at D = 64
+    assert auto(Nq=4096, D=64, smod=T.attn_score_mod(flags=1, slopes=16)) == -13
+    assert auto(B=0) == 0 and auto(Nq=0, ws=None) == 0
+
+
 def test_product_path_does_not_reach_the_oracle():
     """The package and its C sources never import or include the oracle or the workloads."""
     pkg = os.path.join(ROOT, "tiled_attention_attn_amd")

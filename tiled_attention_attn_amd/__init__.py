@@ -5,8 +5,9 @@ softmax, so the N x N score matrix never reaches HBM (the method of
 "FlashAttention 2 principles and PyTorch practice", sections 1 and 3), with the
 mask menu of the FlexAttention / DFlash article: causal, symmetric sliding
 window, document, block-diffusion, BlockMask block sparsity, GQA, and
-split-KV decoding over a paged KV cache merged by log-sum-exp; and the
-backward pass (dQ, dK, dV by recomputation from the saved LSE).
+split-KV decoding over a paged KV cache merged by log-sum-exp, a shape-based
+switch to split-KV for decode-shaped calls; and the backward pass (dQ, dK,
+dV by recomputation from the saved LSE).
 
 The package is a thin ctypes binding over the C ABI of ``include/tiled_attn.h``
 (``libtiled_attn.so``); importing it fails if the library has not been built.
@@ -19,6 +20,7 @@ from ._lib import (  # noqa: F401
     attn_fwd, attn_fwd_blockmask, attn_build_blockmask, attn_blockmask_bytes,
     attn_decode_splitkv, attn_decode_combine, attn_decode_num_splits,
     attn_decode_ws_o_bytes, attn_decode_ws_lse_bytes, attn_bwd, attn_bwd_workspace_bytes,
+    attn_fwd_auto, attn_fwd_auto_plan, attn_auto_plan, PATH_PREFILL, PATH_SPLITKV,
     attn_status_str, attn_abi_version,
     attn_mask_desc, attn_blockmask, lib_handle,
 )

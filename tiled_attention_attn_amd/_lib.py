@@ -63,6 +63,15 @@ SCORE_ALIBI_SYM = 2
 SCORE_REL_BIAS = 4
 
 
+PATH_PREFILL = 0
+PATH_SPLITKV = 1
+
+
+class attn_auto_plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
 class attn_blockmask(ctypes.Structure):
     _fields_ = [
         ("Bm", ctypes.c_int32), ("Hm", ctypes.c_int32),
@@ -96,6 +105,8 @@ def _load():
         "attn_bwd": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
                          I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
         "attn_bwd_workspace_bytes": (S, [I, I, I]),
+        "attn_fwd_auto_plan": (I, [I, I, I, I, I, I, SP, ctypes.POINTER(attn_auto_plan)]),
+        "attn_fwd_auto": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
         "attn_status_str": (ctypes.c_char_p, [I]),
         "attn_abi_version": (I, []),
     }
@@ -110,7 +121,8 @@ _lib = _load()
 EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_blockmask_bytes",
            "attn_decode_splitkv", "attn_decode_combine", "attn_decode_ws_o_bytes",
            "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_status_str", "attn_abi_version")
+           "attn_bwd_workspace_bytes", "attn_fwd_auto_plan", "attn_fwd_auto", "attn_status_str",
+           "attn_abi_version")
 
 
 def _check(func: str, status: int):
@@ -393,6 +405,40 @@ def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=
                        _stream(stream))
     _check("attn_bwd", st)
     return dq, dk, dv
+
+
+def attn_fwd_auto_plan(B, Hq, Hkv, Nq, Nk, D, smod=None) -> attn_auto_plan:
+    """The path attn_fwd_auto takes for a shape (PATH_PREFILL / PATH_SPLITKV), its key split
+    count and the workspace bytes it needs (host only)."""
+    keep_s, sp = _smod_ptr(smod)
+    out = attn_auto_plan()
+    _check("attn_fwd_auto_plan", _lib.attn_fwd_auto_plan(B, Hq, Hkv, Nq, Nk, D, sp, ctypes.byref(out)))
+    return out
+
+
+def attn_fwd_auto(q, k, v, o, lse=None, scale=None, mask=None, workspace=None, stream=None,
+                  smod=None):
+    """attn_fwd with the kernel chosen by shape: split-KV + combine for decode-shaped calls
+    (G * Nq <= 64 query rows per KV head and Nk >= 512), the prefill kernels otherwise.
+    ``workspace`` is a CUDA tensor of at least attn_fwd_auto_plan(...).workspace_bytes bytes
+    (allocated here if None)."""
+    dt = _half(q, k, v, o)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
+    if workspace is None:
+        need = attn_fwd_auto_plan(B, Hq, Hkv, Nq, Nk, D, smod).workspace_bytes
+        workspace = torch.empty(max((need + 3) // 4, 1), dtype=torch.float32, device=q.device)
+    if not workspace.is_contiguous():
+        raise TypeError("workspace must be contiguous")
+    st = _lib.attn_fwd_auto(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                            _ptr(o), _strides(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, dt, scale, mp,
+                            sp, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream))
+    _check("attn_fwd_auto", st)
+    return o, lse
 
 
 def attn_status_str(status: int) -> str:

@@ -146,11 +146,48 @@ void set_slots(FwdParams& p, bool paired) {
   p.xcd_remap = (units % 8) == 0;
 }
 
+// Shape-based choice of attn_fwd_auto.  A decode-shaped call -- all G * Nq
+// query rows of a KV head fit one 64-row group of the split-KV kernel, and
+// there are at least kAutoMinKeys keys -- runs split-KV + combine: K/V are
+// read once per KV head instead of once per query head, and the key splits
+// fill the GPU even when B * Hkv cannot.  A relative-position bias table
+// (not offered by the split-KV kernel) keeps the call on the prefill kernels.
+constexpr int kAutoMinKeys = 512;
+constexpr int kAutoSplitKeys = 256;  // fewest keys per split
+constexpr long kAutoTargetGroups = 2L * 256;  // two work groups per CU on 256 CUs
+
+struct AutoPlan {
+  int path, S, chunk;
+  size_t ws_o_bytes, ws_bytes;
+};
+
+AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_score_mod* smod) {
+  AutoPlan pl{ATTN_PATH_PREFILL, 0, 0, 0, 0};
+  const long rows = (long)(Hq / Hkv) * Nq;
+  const bool rel = smod != nullptr && (smod->flags & ATTN_SCORE_REL_BIAS) != 0;
+  if (Nq < 1 || rows > 64 || Nk < kAutoMinKeys || rel) return pl;
+  const long units = (long)B * Hkv;
+  long S = units > 0 ? (kAutoTargetGroups + units - 1) / units : 1;
+  const long max_s = Nk / kAutoSplitKeys;
+  if (S > max_s) S = max_s;
+  if (S < 1) S = 1;
+  // keys per split, a whole number of 64-key steps; no split left empty
+  const long chunk = ((Nk + S - 1) / S + 63) / 64 * 64;
+  S = (Nk + chunk - 1) / chunk;
+  pl.path = ATTN_PATH_SPLITKV;
+  pl.S = (int)S;
+  pl.chunk = (int)chunk;
+  const size_t parts = (size_t)B * Hq * Nq * S;
+  pl.ws_o_bytes = (parts * D * sizeof(float) + 255) / 256 * 256;
+  pl.ws_bytes = pl.ws_o_bytes + parts * sizeof(float);
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
 
-int attn_abi_version(void) { return 4; }
+int attn_abi_version(void) { return 5; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -304,6 +341,9 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
   p.kc = k_cache;
   p.vc = v_cache;
+  p.k_sb = p.v_sb = 0;
+  p.k_sh = p.v_sh = D;
+  p.k_sn = p.v_sn = (int64_t)Hkv * D;
   p.bt = block_table;
   p.bt_stride = bt_stride;
   p.seq_lens = seq_lens;
@@ -334,6 +374,65 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, i
   if (!aligned16(o) || !aligned16(ws_o)) return ATTN_ERR_ALIGN;
   if (B == 0 || Hq == 0 || Lq == 0) return ATTN_OK;
   return launch_combine(ws_o, ws_lse, B, Hq, Lq, S, D, dtype, o, o_stride[0], o_stride[1],
+                        o_stride[2], lse, stream);
+}
+
+int attn_fwd_auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                       const attn_score_mod* smod, attn_auto_plan* out) {
+  if (out == nullptr) return ATTN_ERR_NULL;
+  *out = attn_auto_plan{ATTN_PATH_PREFILL, 0, 0};
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  AutoPlan pl = auto_plan(B, Hq, Hkv, Nq, Nk, D, smod);
+  out->path = pl.path;
+  out->num_splits = pl.S;
+  out->workspace_bytes = pl.ws_bytes;
+  return ATTN_OK;
+}
+
+int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
+                  const int64_t k_stride[3], const void* v, const int64_t v_stride[3], void* o,
+                  const int64_t o_stride[3], float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                  int D, int dtype, float scale, const attn_mask_desc* mask,
+                  const attn_score_mod* smod, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int st = check_common(q, q_stride, k, k_stride, v, v_stride, o, o_stride, B, Hq, Hkv, Nq, Nk,
+                        D, dtype, scale);
+  if (st) return st;
+  const AutoPlan pl = auto_plan(B, Hq, Hkv, Nq, Nk, D, smod);
+  if (pl.path == ATTN_PATH_PREFILL)
+    return attn_fwd(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk,
+                    D, dtype, scale, mask, smod, stream);
+  DecParams p;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_smod(smod, false, 0, false, p.smod))) return st;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (workspace == nullptr) return ATTN_ERR_NULL;
+  if (workspace_bytes < pl.ws_bytes) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  const int G = Hq / Hkv;
+  p.q = q;
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.kc = k;
+  p.vc = v;
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
+  p.bt = nullptr;
+  p.bt_stride = 0;
+  p.seq_lens = nullptr;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G; p.Lq = Nq; p.ps = 1; p.S = pl.S;
+  p.chunk = pl.chunk;
+  p.max_keys = Nk;
+  p.num_pages = 1;
+  p.rows = G * Nq;
+  p.n_rg = (p.rows + 63) / 64;
+  p.c2 = scale * 1.4426950408889634f;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
+  if ((st = launch_decode(p, D, dtype, stream))) return st;
+  return launch_combine(p.ws_o, p.ws_lse, B, Hq, Nq, pl.S, D, dtype, o, o_stride[0], o_stride[1],
                         o_stride[2], lse, stream);
 }
 

@@ -10,6 +10,10 @@
 // (D=128) with an online softmax (running max, exp-sum, rescaled
 // accumulator), and the split's normalised partial O_s and LSE_s go to an
 // fp32 workspace.  The combine kernel then merges the splits by their LSE.
+// The same kernel also takes contiguous, strided K/V [B, Hkv, Nk, D] (no
+// block table): the split-KV half of the shape-based choice that the same
+// article describes, where a decode-shaped call switches from the prefill
+// kernel to split-KV.
 //
 // gfx950 mapping:
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 / _f16 (16 keys x
@@ -50,7 +54,7 @@ __device__ __forceinline__ uint32_t dec_tile_off(uint32_t row, uint32_t chunk) {
 
 __device__ __forceinline__ float xor_lane(float x, int m) { return __shfl_xor(x, m, 64); }
 
-template <int D, typename T, bool SM>
+template <int D, typename T, bool SM, bool PAGED>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(const DecParams p) {
   constexpr int kDecKBlk = DecKBlk<D>::value;
@@ -76,8 +80,9 @@ decode_kernel(const DecParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
 
-  // Sequence length as given, clamped to what the block table can address.
-  const int seq_len = min(max(p.seq_lens[b], 0), p.max_keys);
+  // Sequence length as given, clamped to what the block table can address;
+  // contiguous K/V have max_keys keys in every sequence.
+  const int seq_len = PAGED ? min(max(p.seq_lens[b], 0), p.max_keys) : p.max_keys;
   const int k_begin = s * p.chunk;
   const int k_end = min(seq_len, k_begin + p.chunk);
 
@@ -133,17 +138,21 @@ decode_kernel(const DecParams p) {
   }
   // The split's block-table entries go to LDS once, so the pipelined loop
   // below issues no vector-memory loads other than the K/V copies.
-  const int32_t* bt_row = p.bt + b * p.bt_stride;
-  const int page0 = k_begin / p.ps;
-  const int n_split_pages = k_end > k_begin ? (k_end - 1) / p.ps - page0 + 1 : 0;
-  for (int i = tid; i < n_split_pages; i += kDecThreads) {
-    const int page = bt_row[page0 + i];
-    s_pages[i] = page < 0 ? 0 : (page >= p.num_pages ? (int)p.num_pages - 1 : page);
+  int page0 = 0, n_split_pages = 0;
+  if constexpr (PAGED) {
+    const int32_t* bt_row = p.bt + b * p.bt_stride;
+    page0 = k_begin / p.ps;
+    n_split_pages = k_end > k_begin ? (k_end - 1) / p.ps - page0 + 1 : 0;
+    for (int i = tid; i < n_split_pages; i += kDecThreads) {
+      const int page = bt_row[page0 + i];
+      s_pages[i] = page < 0 ? 0 : (page >= p.num_pages ? (int)p.num_pages - 1 : page);
+    }
   }
   wait_vmem();  // Q fragments and page entries
   __syncthreads();
 
-  const int64_t row_stride = (int64_t)p.Hkv * D;  // elements between slots of a page
+  const T* kbh = static_cast<const T*>(p.kc) + kvh * p.k_sh + (PAGED ? 0 : b * p.k_sb);
+  const T* vbh = static_cast<const T*>(p.vc) + kvh * p.v_sh + (PAGED ? 0 : b * p.v_sb);
   auto issue = [&](int kb, int st) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
@@ -153,13 +162,16 @@ decode_kernel(const DecParams p) {
       const uint32_t chunk = (slot % CPR) ^ DecSwz<D>::f(row);
       int key = kb + (int)row;
       key = key < k_end ? key : k_end - 1;
-      int pidx = key / p.ps - page0;  // in [0, n_split_pages) for every issued step
-      pidx = pidx < 0 ? 0 : (pidx >= n_split_pages ? n_split_pages - 1 : pidx);
-      const int page = s_pages[pidx];
-      const int64_t off = ((int64_t)page * p.ps + key % p.ps) * row_stride + kvh * D + chunk * 8;
+      // the key's pool slot (paged) or its row (contiguous)
+      int64_t slot_k = key;
+      if constexpr (PAGED) {
+        int pidx = key / p.ps - page0;  // in [0, n_split_pages) for every issued step
+        pidx = pidx < 0 ? 0 : (pidx >= n_split_pages ? n_split_pages - 1 : pidx);
+        slot_k = (int64_t)s_pages[pidx] * p.ps + key % p.ps;
+      }
       const uint32_t loff = __builtin_amdgcn_readfirstlane(inst * 1024);
-      dma16(static_cast<const T*>(p.kc) + off, lds_addr(bufK(st)) + loff);
-      dma16(static_cast<const T*>(p.vc) + off, lds_addr(bufV(st)) + loff);
+      dma16(kbh + slot_k * p.k_sn + chunk * 8, lds_addr(bufK(st)) + loff);
+      dma16(vbh + slot_k * p.v_sn + chunk * 8, lds_addr(bufV(st)) + loff);
     }
   };
   constexpr int LOADS = 2 * PER_WAVE;  // copies per wave per step
@@ -312,21 +324,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (lse != nullptr && lane == 0) lse[row] = tot > 0.f ? m_use + logf(tot) : kNegInf;
 }
 
-template <typename T, bool SM>
+template <typename T, bool SM, bool PAGED>
 void launch_decode_t(const DecParams& p, int D, dim3 grid, dim3 block, hipStream_t stream) {
-  if (D == 64) hipLaunchKernelGGL((decode_kernel<64, T, SM>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((decode_kernel<128, T, SM>), grid, block, 0, stream, p);
+  if (D == 64) hipLaunchKernelGGL((decode_kernel<64, T, SM, PAGED>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel<128, T, SM, PAGED>), grid, block, 0, stream, p);
 }
 
+template <typename T, bool PAGED>
+void launch_decode_sm(const DecParams& p, int D, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.smod.flags != 0) launch_decode_t<T, true, PAGED>(p, D, grid, block, stream);
+  else launch_decode_t<T, false, PAGED>(p, D, grid, block, stream);
+}
+
+// p.bt == nullptr selects contiguous K/V.
 int launch_decode(const DecParams& p, int D, int dtype, hipStream_t stream) {
   dim3 grid(p.S * p.n_rg, p.Hkv, p.B), block(kDecThreads);
-  const bool sm = p.smod.flags != 0;
+  const bool paged = p.bt != nullptr;
   if (dtype == ATTN_DTYPE_F16) {
-    if (sm) launch_decode_t<f16, true>(p, D, grid, block, stream);
-    else launch_decode_t<f16, false>(p, D, grid, block, stream);
+    if (paged) launch_decode_sm<f16, true>(p, D, grid, block, stream);
+    else launch_decode_sm<f16, false>(p, D, grid, block, stream);
   } else {
-    if (sm) launch_decode_t<bf16, true>(p, D, grid, block, stream);
-    else launch_decode_t<bf16, false>(p, D, grid, block, stream);
+    if (paged) launch_decode_sm<bf16, true>(p, D, grid, block, stream);
+    else launch_decode_sm<bf16, false>(p, D, grid, block, stream);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

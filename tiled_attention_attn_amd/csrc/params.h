@@ -44,15 +44,20 @@ struct BmBuildParams {
   int32_t* full_idx;
 };
 
-// Split-KV paged decode.
+// Split-KV decode, over a paged KV pool (block table) or over contiguous,
+// strided K/V tensors [B, Hkv, Nk, D].
 struct DecParams {
   const void* q;
   int64_t q_sb, q_sh, q_sn;
   const void* kc;
   const void* vc;
-  const int32_t* bt;
+  // Element strides of K and V.  Paged: sn = slot stride inside a page
+  // (Hkv * D), sh = head stride (D), sb unused.  Contiguous: batch, head and
+  // token strides of the caller's tensors.
+  int64_t k_sb, k_sh, k_sn, v_sb, v_sh, v_sn;
+  const int32_t* bt;        // paged only
   int64_t bt_stride;
-  const int32_t* seq_lens;
+  const int32_t* seq_lens;  // paged only; contiguous sequences all have max_keys keys
   int B, Hq, Hkv, G, Lq, ps, S, chunk;  // chunk: keys per split (multiple of ps)
   int rows, n_rg;                       // G*Lq query rows per KV head, groups of 64
   int max_keys;                         // max_pages * page_size
