@@ -17,10 +17,12 @@ with the softmax Jacobian taken row by row:
     dS = P * (dP - rowsum(P * dP))
     dQ = scale * dS K,     dK = scale * dS^T Q
 
-With an additive score_mod (oracle.score_mods: the modified score is
-s + bias(h, q, k)) P is the softmax of the modified scores and, since
-d(s + bias)/ds = 1, the formulas above are unchanged; the bias itself gets no
-gradient here.
+With a score_mod (oracle.score_mods: the modified score is s' = f(s) for
+each (h, q, k)) P is the softmax of the modified scores and dS above is the
+gradient with respect to s'; by the chain rule the gradient with respect to
+s is dS * f'(s).  For the additive changes f'(s) = 1; for softcap
+f(s) = cap tanh(s / cap) and f'(s) = 1 - tanh^2(s / cap).  The bias terms
+and the cap get no gradient here.
 
 GQA (query head hq reads KV head hq // G): dK and dV of a KV head sum the
 contributions of all G query heads that read it.  A row with no visible key
@@ -63,7 +65,9 @@ def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows, score_m
     kk = np.asarray(k[b, kvh], dtype=np.float64)
     vv = np.asarray(v[b, kvh], dtype=np.float64)
     s = _core.scores(qr, kk, scale)
+    jac = None
     if score_mod is not None:
+        jac = _score_mods.dense_dscore(score_mod, b, hq, s, rows, Nk)
         s = _score_mods.dense(score_mod, b, hq, s, rows, Nk)
     if mask_mod is None:
         vis = np.ones_like(s, dtype=bool)
@@ -72,6 +76,8 @@ def bwd_rows(q, k, v, do, scale: float, mask_mod, b: int, hq: int, rows, score_m
     p, _ = _core.masked_softmax(s, vis)
     dp = dor @ vv.T
     ds = softmax_grad(p, dp)
+    if jac is not None:
+        ds = ds * jac
     return scale * (ds @ kk), scale * (ds.T @ qr), p.T @ dor, p, ds
 
 
@@ -81,7 +87,8 @@ def attention_bwd(q, k, v, do, scale: float | None = None, mask_mod=None, row_bl
 
     With ``bound``, also (mQ, mK, mV) of the same shapes: mV = sum_q P |dO|,
     mQ = scale * sum_k m_S |K|, mK = scale * sum_q m_S |Q|, where
-    m_S = |dS| + P * sum_d |dO| (|O| + 2^8 |o_used - O|).
+    m_S = |dS| + P * f'(s) * sum_d |dO| (|O| + 2^8 |o_used - O|), f'(s) = 1 without a
+    score_mod.
     """
     B, Hq, Nq, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
@@ -109,7 +116,12 @@ def attention_bwd(q, k, v, do, scale: float | None = None, mask_mod=None, row_bl
                     if o_used is not None:
                         oerr = np.abs(np.asarray(o_used[b, h], dtype=np.float64)[rows] - o)
                     dterm = np.sum(dor * (np.abs(o) + 256.0 * oerr), axis=-1, keepdims=True)
-                    ms = np.abs(ds) + p * dterm
+                    jac = 1.0
+                    if score_mod is not None:  # the Delta error reaches dS through f'(s) too
+                        sr = _core.scores(np.asarray(q[b, h], dtype=np.float64)[rows],
+                                          np.asarray(k[b, kvh], dtype=np.float64), scale)
+                        jac = _score_mods.dense_dscore(score_mod, b, h, sr, rows, Nk)
+                    ms = np.abs(ds) + p * dterm * jac
                     mq[b, h, rows] = scale * (ms @ np.abs(np.asarray(k[b, kvh], dtype=np.float64)))
                     mk[b, kvh] += scale * (ms.T @ np.abs(np.asarray(q[b, h], dtype=np.float64)[rows]))
                     mv[b, kvh] += p.T @ dor

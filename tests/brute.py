@@ -76,12 +76,21 @@ def _bias(score_spec, h, j, p):
     return add
 
 
+def _cap(score_spec, x):
+    """Tanh capping of the scaled score, applied before the additive terms."""
+    if not score_spec or "softcap" not in score_spec:
+        return x
+    c = score_spec["softcap"]
+    return c * math.tanh(x / c)
+
+
 def attention(q, k, v, scale, spec, score_spec=None):
     """q: nested lists [B][Hq][Nq][D]; k, v: [B][Hkv][Nk][D].  Returns (O, LSE) nested lists.
 
     score_spec (optional) adds to each scaled score: "alibi": slopes per head
     (+ slope (j - p)), "alibi_sym": slopes (- slope |j - p|), "rel": (table, R)
-    (+ table[h][clamp(j - p, -R, R) + R])."""
+    (+ table[h][clamp(j - p, -R, R) + R]), "softcap": cap (the scaled score becomes
+    cap * tanh(score / cap) before the additive terms)."""
     B, Hq = len(q), len(q[0])
     Hkv = len(k[0])
     Nq, Nk = len(q[0][0]), len(k[0][0])
@@ -100,7 +109,7 @@ def attention(q, k, v, scale, spec, score_spec=None):
                     Lh.append(-math.inf)
                     continue
                 pos = i + (Nk - Nq)
-                s = {j: scale * math.fsum(a * c for a, c in zip(q[b][h][i], k[b][kv][j]))
+                s = {j: _cap(score_spec, scale * math.fsum(a * c for a, c in zip(q[b][h][i], k[b][kv][j])))
                      + _bias(score_spec, h, j, pos) for j in keys}
                 m = max(s.values())
                 e = {j: math.exp(s[j] - m) for j in keys}

@@ -157,7 +157,7 @@ def _alibi_sign(slopes, Nq, Nk):
 
     def mod(score, b, h, q_idx, kv_idx):
         return score - sl[h] * (np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq)))
-    return mod
+    return OSM._additive(mod)
 
 
 def _alibi_sym_no_abs(slopes, Nq, Nk):
@@ -165,7 +165,7 @@ def _alibi_sym_no_abs(slopes, Nq, Nk):
 
     def mod(score, b, h, q_idx, kv_idx):
         return score - sl[h] * (np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq)))
-    return mod
+    return OSM._additive(mod)
 
 
 def _alibi_top_left(slopes, Nq, Nk):
@@ -173,7 +173,7 @@ def _alibi_top_left(slopes, Nq, Nk):
 
     def mod(score, b, h, q_idx, kv_idx):
         return score + sl[h] * (np.asarray(kv_idx) - np.asarray(q_idx))
-    return mod
+    return OSM._additive(mod)
 
 
 def _rel_bias_unclamped_offset(table, R, Nq, Nk):
@@ -182,7 +182,7 @@ def _rel_bias_unclamped_offset(table, R, Nq, Nk):
     def mod(score, b, h, q_idx, kv_idx):
         d = np.asarray(kv_idx) - (np.asarray(q_idx) + (Nk - Nq))
         return score + tb[h][np.clip(d + R, 0, 2 * R - 1)]
-    return mod
+    return OSM._additive(mod)
 
 
 def _rel_bias_reversed(table, R, Nq, Nk):
@@ -191,7 +191,37 @@ def _rel_bias_reversed(table, R, Nq, Nk):
     def mod(score, b, h, q_idx, kv_idx):
         d = np.asarray(q_idx) + (Nk - Nq) - np.asarray(kv_idx)
         return score + tb[h][np.clip(d, -R, R) + R]
+    return OSM._additive(mod)
+
+
+def _softcap_no_jacobian(cap):
+    m = _orig_softcap(cap)
+    m.dscore = lambda score, b, h, q_idx, kv_idx: np.ones_like(np.asarray(score, dtype=np.float64))
+    return m
+
+
+def _softcap_jacobian_sign(cap):
+    m = _orig_softcap(cap)
+
+    def dscore(score, b, h, q_idx, kv_idx):
+        t = np.tanh(np.asarray(score, dtype=np.float64) / cap)
+        return 1.0 + t * t
+    m.dscore = dscore
+    return m
+
+
+def _softcap_no_cap_factor(cap):
+    def mod(score, b, h, q_idx, kv_idx):
+        return np.tanh(np.asarray(score, dtype=np.float64) / cap)
+
+    def dscore(score, b, h, q_idx, kv_idx):
+        t = np.tanh(np.asarray(score, dtype=np.float64) / cap)
+        return (1.0 - t * t) / cap
+    mod.dscore = dscore
     return mod
+
+
+_orig_softcap = OSM.softcap
 
 
 MUTANTS = {
@@ -218,6 +248,9 @@ MUTANTS = {
     "alibi_top_left": (OSM, "alibi", _alibi_top_left),
     "rel_bias_clamp_off_by_one": (OSM, "rel_bias", _rel_bias_unclamped_offset),
     "rel_bias_reversed_distance": (OSM, "rel_bias", _rel_bias_reversed),
+    "softcap_jacobian_dropped": (OSM, "softcap", _softcap_no_jacobian),
+    "softcap_jacobian_sign": (OSM, "softcap", _softcap_jacobian_sign),
+    "softcap_cap_factor_dropped": (OSM, "softcap", _softcap_no_cap_factor),
 }
 
 

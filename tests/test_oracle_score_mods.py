@@ -9,6 +9,11 @@
   table that is one large entry selects a single key
 * identities: slope 0 is no change; a constant table shifts LSE by the
   constant and leaves O alone
+* softcap (cap * tanh(score / cap), applied before the additive terms):
+  brute force with math.tanh; central finite differences of the brute-force
+  loss for the gradients (this pins the chain-rule factor 1 - tanh^2); the
+  saturated closed form LSE = log(n+ e^cap + n- e^-cap) when every score is
+  far beyond +-cap; a cap far above every score is no change
 """
 import math
 import zlib
@@ -28,6 +33,8 @@ SLOPES4 = [0.5, 0.25, 0.125, 0.0625]
 
 def _oracle_smod(sspec, Nq, Nk):
     mods = []
+    if "softcap" in sspec:
+        mods.append(SM.softcap(sspec["softcap"]))
     if "alibi" in sspec:
         mods.append(SM.alibi(sspec["alibi"], Nq, Nk))
     if "alibi_sym" in sspec:
@@ -164,7 +171,92 @@ def test_score_identities():
     pin_score_identities()
 
 
+SOFTCAP_BRUTE = [
+    # (name, B, Hq, Hkv, Nq, Nk, D, mask spec, score spec)
+    ("softcap_causal", 1, 2, 1, 7, 7, 3, {"causal": True}, {"softcap": 0.8}),
+    ("softcap_alibi_sym_window", 1, 1, 1, 9, 9, 2, {"window": (3, 3)}, {"softcap": 1.5, "alibi_sym": [0.7]}),
+    ("softcap_rel_bottom_right", 1, 2, 2, 3, 8, 3, {"causal": True},
+     {"softcap": 0.5, "rel": ([[0.1, -0.4, 0.9, 0.3, -1.2], [2.0, 0.0, -0.5, 0.25, 1.5]], 2)}),
+]
+
+
+@pytest.mark.parametrize("case", SOFTCAP_BRUTE, ids=[c[0] for c in SOFTCAP_BRUTE])
+def test_softcap_brute_force(case):
+    pin_score_brute(case)
+
+
+SOFTCAP_FD = [
+    # (name, Hq, Hkv, Nq, Nk, D, mask spec, score spec)
+    ("softcap_gqa_bottom_right", 2, 1, 3, 5, 3, {"causal": True}, {"softcap": 0.7}),
+    ("softcap_alibi_window", 1, 1, 5, 5, 2, {"window": (2, 2)}, {"softcap": 1.2, "alibi": [0.4]}),
+]
+
+
+def _brute_loss_smod(q, k, v, do, scale, spec, sspec):
+    o, _ = brute.attention(q.tolist(), k.tolist(), v.tolist(), scale, spec, sspec)
+    return math.fsum(a * c for a, c in zip(np.asarray(o).ravel().tolist(), do.ravel().tolist()))
+
+
+def pin_softcap_finite_differences():
+    for name, Hq, Hkv, Nq, Nk, D, mspec, sspec in SOFTCAP_FD:
+        seed = zlib.crc32(name.encode()) % 1000
+        q, k, v = _tiny(seed, 1, Hq, Hkv, Nq, Nk, D)
+        q *= 2.0  # scores of a few units: well into the curved part of tanh at these caps
+        do = _rand(seed + 1, (1, Hq, Nq, D))
+        scale = 1.0 / math.sqrt(D)
+        dq, dk, dv = OBW.attention_bwd(q, k, v, do, scale, _oracle_mod(mspec, Nq, Nk, 1), row_block=2,
+                                       score_mod=_oracle_smod(sspec, Nq, Nk))
+        h = 1e-5
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                x0 = x[idx]
+                x[idx] = x0 + h
+                fp = _brute_loss_smod(q, k, v, do, scale, mspec, sspec)
+                x[idx] = x0 - h
+                fm = _brute_loss_smod(q, k, v, do, scale, mspec, sspec)
+                x[idx] = x0
+                fd[idx] = (fp - fm) / (2 * h)
+            assert np.max(np.abs(fd - g)) < 1e-7, (name, np.max(np.abs(fd - g)))
+
+
+def test_softcap_finite_differences():
+    pin_softcap_finite_differences()
+
+
+def pin_softcap_closed_forms():
+    # Saturation: q = (A, 0, ...) and keys (+-1, x, ...) give scores +-scale A = +-50 cap, where
+    # tanh is +-1 to within 1e-40: LSE_p = log(n+ e^cap + n- e^-cap) over the keys up to p.
+    N, D, cap = 12, 4, 2.0
+    rng = np.random.default_rng(9)
+    sign = np.where(rng.random(N) < 0.5, 1.0, -1.0)
+    sign[0] = 1.0
+    k = rng.normal(size=(1, 1, N, D))
+    k[0, 0, :, 0] = sign
+    v = rng.normal(size=(1, 1, N, D))
+    scale = 0.5
+    q = np.zeros((1, 1, N, D))
+    q[0, 0, :, 0] = 50.0 * cap / scale
+    o, lse = oracle.attention(q, k, v, scale, M.causal(N, N), score_mod=SM.softcap(cap))
+    for p in range(N):
+        npos = int((sign[:p + 1] > 0).sum())
+        nneg = p + 1 - npos
+        assert abs(lse[0, 0, p] - math.log(npos * math.exp(cap) + nneg * math.exp(-cap))) < 1e-12
+        w = np.where(sign[:p + 1] > 0, math.exp(cap), math.exp(-cap))
+        assert np.max(np.abs(o[0, 0, p] - (w[:, None] * v[0, 0, :p + 1]).sum(0) / w.sum())) < 1e-12
+    # A cap far above every score: cap tanh(s / cap) = s - s^3 / (3 cap^2) + ..., no change to 1e-9.
+    q2, k2, v2 = _tiny(56, 1, 2, 1, 30, 30, 8)
+    base = oracle.attention(q2, k2, v2, 0.4, M.causal(30, 30))
+    big = oracle.attention(q2, k2, v2, 0.4, M.causal(30, 30), score_mod=SM.softcap(1e6))
+    assert np.max(np.abs(big[0] - base[0])) < 1e-9 and np.max(np.abs(big[1] - base[1])) < 1e-9
+
+
+def test_softcap_closed_forms():
+    pin_softcap_closed_forms()
+
+
 SCORE_PINS = [
-    lambda: [pin_score_brute(c) for c in SCORE_BRUTE],
+    lambda: [pin_score_brute(c) for c in SCORE_BRUTE + SOFTCAP_BRUTE],
     pin_score_sdpa, pin_score_closed_forms, pin_score_identities,
+    pin_softcap_finite_differences, pin_softcap_closed_forms,
 ]
