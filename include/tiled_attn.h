@@ -109,30 +109,36 @@ typedef struct attn_mask_desc {
 } attn_mask_desc;
 
 /* ---- score modification -------------------------------------------------
- * Additive changes of the scaled score before the softmax, the score_mod of
- * the FlexAttention article (section 1: ALiBi, a position bias, a learnable
- * bias).  With d = k - p (key index minus the query's aligned position):
- *     ALIBI      score + slopes[hq] * d          (<= 0 where k <= p)
- *     ALIBI_SYM  score - slopes[hq] * |d|
- *     REL_BIAS   score + rel_bias[hq][clamp(d, -R, R) + R]
- * ALIBI and ALIBI_SYM exclude each other; REL_BIAS combines with either.
- * LSE is then the log-sum-exp of the changed scores.  The bias arrays are
- * device memory; the backward pass treats them as constants (no gradient).
+ * Changes of the scaled score before the softmax, the score_mod of the
+ * FlexAttention article (section 1: ALiBi, a position bias, a learnable
+ * bias), plus tanh capping.  With s = scale * q.k and d = k - p (key index
+ * minus the query's aligned position), the score becomes
+ *     SOFTCAP    s -> softcap * tanh(s / softcap)      (applied first)
+ *     ALIBI      + slopes[hq] * d                      (<= 0 where k <= p)
+ *     ALIBI_SYM  - slopes[hq] * |d|
+ *     REL_BIAS   + rel_bias[hq][clamp(d, -R, R) + R]
+ * ALIBI and ALIBI_SYM exclude each other; the others combine freely.  LSE is
+ * then the log-sum-exp of the changed scores.  The bias arrays are device
+ * memory; the backward pass applies the cap's derivative 1 - tanh^2(s / cap)
+ * and treats the biases and the cap as constants (no gradient for them).
+ * SOFTCAP needs a finite softcap > 0.
  * REL_BIAS needs 0 <= R <= 1023 and, in attn_bwd, (Hq / Hkv) * (2R + 1) <=
- * 8192; attn_decode_splitkv takes ALIBI / ALIBI_SYM only.  attn_fwd,
+ * 8192; attn_decode_splitkv takes ALIBI / ALIBI_SYM / SOFTCAP only.  attn_fwd,
  * attn_fwd_blockmask and attn_bwd take a score change at D = 128 only
  * (ATTN_ERR_SCORE_MOD at D = 64).
  */
 #define ATTN_SCORE_ALIBI 1u
 #define ATTN_SCORE_ALIBI_SYM 2u
 #define ATTN_SCORE_REL_BIAS 4u
-#define ATTN_SCORE_ALL 7u
+#define ATTN_SCORE_SOFTCAP 8u
+#define ATTN_SCORE_ALL 15u
 
 typedef struct attn_score_mod {
   uint32_t flags;         /* ATTN_SCORE_* bits (0 = no change)                    */
   const float* slopes;    /* ALIBI / ALIBI_SYM: device float [Hq]                 */
   const float* rel_bias;  /* REL_BIAS: device float [Hq][2 * rel_radius + 1]      */
   int32_t rel_radius;     /* REL_BIAS: R                                          */
+  float softcap;          /* SOFTCAP: the cap (> 0)                               */
 } attn_score_mod;
 
 /* ---- dense-mask prefill ---------------------------------------------------

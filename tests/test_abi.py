@@ -70,7 +70,10 @@ def test_fwd_argument_errors(T):
     SMD = T.attn_score_mod
     qs128 = (128 * 256, 128 * 256, 128)
     f128 = lambda **kw: _fwd(T, D=128, qs=qs128, **kw)
-    assert f128(smod=SMD(flags=8)) == -13                                    # unknown flag
+    assert f128(smod=SMD(flags=16)) == -13                                   # unknown flag
+    for cap in (0.0, -3.0, float("inf"), float("nan")):                      # SOFTCAP needs a cap > 0
+        assert f128(smod=SMD(flags=8, softcap=cap)) == -13
+    assert _fwd(T, smod=SMD(flags=8, softcap=30.0)) == -13                   # not at D = 64
     assert f128(smod=SMD(flags=3, slopes=16)) == -13                         # ALIBI and ALIBI_SYM
     assert f128(smod=SMD(flags=1, slopes=None)) == -1
     assert f128(smod=SMD(flags=4, rel_bias=None, rel_radius=3)) == -1
@@ -130,6 +133,7 @@ def test_blockmask_and_decode_argument_errors(T):
     assert dec(D=80) == -3
     assert dec(dt=5) == -12
     assert dec(smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=2)) == -13  # no table in decode
+    assert dec(smod=T.attn_score_mod(flags=8, softcap=0.0)) == -13
     assert dec(Hq=3) == -4
     md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=1, doc_stride=2)
     assert dec(mask=md) == -7

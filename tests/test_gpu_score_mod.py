@@ -1,6 +1,6 @@
-"""GPU parity: additive score changes (ALiBi, symmetric ALiBi, relative-position
-bias table) in prefill, BlockMask prefill, paged decode and the backward pass,
-against the fp64 oracle with the same score_mod."""
+"""GPU parity: score changes (tanh soft-capping, ALiBi, symmetric ALiBi,
+relative-position bias table) in prefill, BlockMask prefill, paged decode and
+the backward pass, against the fp64 oracle with the same score_mod."""
 import math
 import zlib
 
@@ -13,7 +13,7 @@ from oracle import backward as OBW, masks as M, paged as OP, score_mods as SM
 import workloads as W
 from gpu_util import f64, assert_close, announce
 from test_gpu_prefill import _mask_pair
-from test_gpu_backward import _fwd_bwd, assert_grad_close
+from test_gpu_backward import _fwd_bwd, assert_grad_close, fp16_floor
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +34,17 @@ def alibi_slopes(H):
     return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
 
 
+# Cap of the "cap" kinds: N(0,1) inputs give scores of about +-1..3, where
+# tanh(s / 2) is well away from linear.
+CAP = 2.0
+
+
 def _smod_pair(kind, Hq, Nq, Nk, R=64, seed=0):
     """(GPU ScoreMod, oracle score_mod, tensors kept alive) for a kind string."""
     mods, keep, gm = [], [], T.ScoreMod()
+    if "cap" in kind:  # applied first, as the library does
+        gm.softcap = CAP
+        mods.append(SM.softcap(CAP))
     if "alibi" in kind:
         sl = alibi_slopes(Hq)
         keep.append(sl.to(DEV))
@@ -61,6 +69,10 @@ PREFILL = [
     ("rel_alibi_sym_docs_d128", 2, 2, 2, 520, 520, 128, {"docs": [[130, 250, 140], [520]]}, "alibi_sym+rel"),
     ("alibi_bottom_right_d64", 1, 2, 2, 100, 500, 64, {"causal": True}, "alibi"),
     ("rel_causal_d128_ragged", 1, 2, 1, 333, 333, 128, {"causal": True}, "rel"),
+    ("cap_causal_d128", 1, 2, 2, 600, 600, 128, {"causal": True}, "cap"),
+    ("cap_alibi_sym_window_d128_gqa", 1, 4, 2, 700, 700, 128, {"window": (200, 200)}, "cap+alibi_sym"),
+    ("cap_rel_bottom_right_d128", 1, 2, 1, 200, 500, 128, {"causal": True}, "cap+rel"),
+    ("cap_d64", 1, 2, 2, 300, 300, 64, {"causal": True}, "cap"),
 ]
 
 
@@ -70,7 +82,8 @@ def test_prefill_score_mod(case, dtype):
     name, B, Hq, Hkv, Nq, Nk, D, mspec, kind = case
     if D == 64:
         pytest.skip(D64_OFF)
-    if dtype == torch.float16 and name not in ("alibi_causal_d128", "rel_alibi_sym_docs_d128"):
+    if dtype == torch.float16 and name not in ("alibi_causal_d128", "rel_alibi_sym_docs_d128",
+                                               "cap_alibi_sym_window_d128_gqa"):
         pytest.skip("fp16 checked on a subset")
     announce(f"score_mod prefill {name} {dtype}")
     g = W.generator(zlib.crc32(name.encode()) % 9973)
@@ -98,8 +111,9 @@ def test_d64_score_change_rejected():
     assert e.value.status == -13
 
 
-def test_blockmask_score_mod():
-    announce("score_mod blockmask")
+@pytest.mark.parametrize("kind", ["alibi+rel", "cap+alibi+rel"])
+def test_blockmask_score_mod(kind):
+    announce(f"score_mod blockmask {kind}")
     D, Hq, Hkv, N = 128, 4, 2, 900
     g = W.generator(77)
     q = W.randn_bf16(g, (1, Hq, N, D))
@@ -109,7 +123,7 @@ def test_blockmask_score_mod():
     tm = W.blockmask_tile_map(g, nt, 0.3)
     bm = T.BlockMask(1, 1, N, N)
     T.attn_build_blockmask(bm, 1, N, N, tile_map=tm[None, None].contiguous().to(DEV))
-    sg, smod, keep = _smod_pair("alibi+rel", Hq, N, N, R=100, seed=3)
+    sg, smod, keep = _smod_pair(kind, Hq, N, N, R=100, seed=3)
     qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
     o = torch.empty_like(qg)
     lse = torch.empty(1, Hq, N, dtype=torch.float32, device=DEV)
@@ -117,7 +131,7 @@ def test_blockmask_score_mod():
     torch.cuda.synchronize()
     mod = M.blockmask(tm.numpy(), 128, M.causal(N, N))
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), 1 / math.sqrt(D), mod, score_mod=smod)
-    assert_close(f64(o), f64(lse), ro, rl, "blockmask score_mod")
+    assert_close(f64(o), f64(lse), ro, rl, f"blockmask score_mod {kind}")
 
 
 def test_alibi_closed_form_q0():
@@ -144,11 +158,38 @@ def test_alibi_closed_form_q0():
         assert err < 2e-5, (h, err)
 
 
+def test_softcap_saturated_closed_form():
+    """Scores of +-90 (q = (1024, 0, ...), keys (+-1, ...), scale 1/sqrt(128)) saturate the
+    cap of 2 exactly, so row p's LSE is log(n+ e^2 + n- e^-2) over its keys: a key lost or
+    counted twice moves it by about 1/n."""
+    announce("softcap closed form")
+    N, D, H = 700, 128, 2
+    g = W.generator(12)
+    k = W.randn_bf16(g, (1, H, N, D))
+    v = W.randn_bf16(g, (1, H, N, D))
+    sign = torch.where(torch.rand(N, generator=torch.Generator().manual_seed(4)) < 0.3, -1.0, 1.0)
+    k[0, :, :, 0] = sign.to(torch.bfloat16)
+    q = torch.zeros(1, H, N, D, dtype=torch.bfloat16)
+    q[..., 0] = 1024.0
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.empty_like(qg)
+    lse = torch.empty(1, H, N, dtype=torch.float32, device=DEV)
+    T.attn_fwd(qg, kg, vg, o, lse, 1 / math.sqrt(D), T.Mask(causal=True), smod=T.ScoreMod(softcap=CAP))
+    torch.cuda.synchronize()
+    npos = np.cumsum(sign.numpy() > 0)
+    nneg = np.arange(1, N + 1) - npos
+    want = np.log(npos * math.exp(CAP) + nneg * math.exp(-CAP))
+    err = np.max(np.abs(lse.cpu().numpy() - want[None, None]))
+    assert err < 2e-5, err
+
+
 DECODE = [
     # (id, B, Hq, Hkv, Lq, Nk, D, seq_lens, S, mask, kind)
     ("alibi_causal", 2, 8, 2, 5, 300, 128, [300, 171], 3, None, "alibi"),
     ("alibi_sym_window", 2, 4, 2, 8, 3000, 128, [3000, 2500], 4, (2048, 2048), "alibi_sym"),
     ("alibi_d64_gqa8", 1, 8, 1, 4, 333, 64, [333], 5, None, "alibi"),
+    ("cap_causal", 2, 8, 2, 5, 300, 128, [300, 171], 3, None, "cap"),
+    ("cap_alibi_d64_gqa8", 1, 8, 1, 4, 333, 64, [333], 5, None, "cap+alibi"),
 ]
 
 
@@ -161,7 +202,10 @@ def test_decode_score_mod(case):
                         seed=11 + len(name), seq_lens=sl)
     t = wl.tensors
     slopes = alibi_slopes(Hq)
-    sg = T.ScoreMod(alibi_slopes=slopes.to(DEV), symmetric="sym" in kind)
+    kw = {"softcap": CAP} if "cap" in kind else {}
+    if "alibi" in kind:
+        kw.update(alibi_slopes=slopes.to(DEV), symmetric="sym" in kind)
+    sg = T.ScoreMod(**kw)
     ws_o = torch.empty(B, Hq, Lq, S, D, dtype=torch.float32, device=DEV)
     ws_l = torch.empty(B, Hq, Lq, S, dtype=torch.float32, device=DEV)
     gmask = T.Mask(window=win) if win else None
@@ -176,7 +220,10 @@ def test_decode_score_mod(case):
         kl = OP.gather(kp, bt, b, sl[b])[None]
         vl = OP.gather(vp, bt, b, sl[b])[None]
         mod = M.window(win[0], win[1], Lq, sl[b]) if win else M.causal(Lq, sl[b])
-        smod = (SM.alibi_sym if "sym" in kind else SM.alibi)(slopes.double().numpy(), Lq, sl[b])
+        mods = [SM.softcap(CAP)] if "cap" in kind else []
+        if "alibi" in kind:
+            mods.append((SM.alibi_sym if "sym" in kind else SM.alibi)(slopes.double().numpy(), Lq, sl[b]))
+        smod = SM.combine(*mods)
         ro, rl = oracle.attention(f64(t["q"])[b:b + 1], kl, vl, wl.scale, mod, score_mod=smod)
         assert_close(f64(o[b:b + 1]), f64(lse[b:b + 1]), ro, rl, f"{name} b{b}")
 
@@ -187,6 +234,10 @@ BACKWARD = [
     ("rel_causal_d128", 1, 2, 1, 400, 400, 128, {"causal": True}, "rel", "bf16"),
     ("alibi_sym_window_d64", 1, 2, 2, 600, 600, 64, {"window": (50, 50)}, "alibi_sym+rel", "bf16"),
     ("alibi_causal_d128_fp16", 1, 2, 2, 300, 300, 128, {"causal": True}, "alibi", "fp16"),
+    ("cap_causal_d128", 1, 2, 1, 400, 400, 128, {"causal": True}, "cap", "bf16"),
+    ("cap_alibi_sym_rel_window_d128_gqa", 1, 4, 2, 500, 500, 128, {"window": (60, 60)}, "cap+alibi_sym+rel",
+     "bf16"),
+    ("cap_d128_fp16", 1, 2, 2, 300, 300, 128, {"causal": True}, "cap", "fp16"),
 ]
 
 
@@ -217,6 +268,7 @@ def test_backward_score_mod(case):
     rq, rk, rv, (mq, mk, mv) = OBW.attention_bwd(f64(q), f64(k), f64(v), f64(do), scale, mod,
                                                  row_block=256, bound=True, o_used=f64(o),
                                                  score_mod=smod)
-    assert_grad_close(f64(dq), rq, mq, f"{name} dQ")
-    assert_grad_close(f64(dk), rk, mk, f"{name} dK")
-    assert_grad_close(f64(dv), rv, mv, f"{name} dV")
+    fq, fk, fv = fp16_floor(f64(q), f64(k), f64(do), scale, mod) if dt == "fp16" else (0.0,) * 3
+    assert_grad_close(f64(dq), rq, mq, f"{name} dQ", fq)
+    assert_grad_close(f64(dk), rk, mk, f"{name} dK", fk)
+    assert_grad_close(f64(dv), rv, mv, f"{name} dV", fv)

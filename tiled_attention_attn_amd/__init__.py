@@ -14,7 +14,7 @@ The package is a thin ctypes binding over the C ABI of ``include/tiled_attn.h``
 """
 from ._lib import (  # noqa: F401
     AttnError, Mask, ScoreMod, BlockMask, LIB_PATH, EXPORTS, DTYPE_BF16, DTYPE_F16,
-    SCORE_ALIBI, SCORE_ALIBI_SYM, SCORE_REL_BIAS, attn_score_mod,
+    SCORE_ALIBI, SCORE_ALIBI_SYM, SCORE_REL_BIAS, SCORE_SOFTCAP, attn_score_mod,
     MASK_CAUSAL, MASK_WINDOW, MASK_DOCUMENT, MASK_BLOCK_CAUSAL, BLOCKMASK_TILE,
     TILE_EMPTY, TILE_PARTIAL, TILE_FULL,
     attn_fwd, attn_fwd_blockmask, attn_build_blockmask, attn_blockmask_bytes,

@@ -55,12 +55,14 @@ class attn_score_mod(ctypes.Structure):
         ("slopes", ctypes.c_void_p),
         ("rel_bias", ctypes.c_void_p),
         ("rel_radius", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
     ]
 
 
 SCORE_ALIBI = 1
 SCORE_ALIBI_SYM = 2
 SCORE_REL_BIAS = 4
+SCORE_SOFTCAP = 8
 
 
 PATH_PREFILL = 0
@@ -209,20 +211,26 @@ def _mask_ptr(mask):
 
 @dataclass
 class ScoreMod:
-    """Additive score changes of attn_score_mod (d = key index - query position):
+    """Score changes of attn_score_mod (s = scale * q.k, d = key index - query position):
 
+    softcap: float > 0 -> s becomes softcap * tanh(s / softcap), before the additive terms;
     alibi_slopes: float32 [Hq] on the GPU -> + slope * d (or - slope * |d| with
     symmetric=True);  rel_bias: float32 [Hq, 2R+1] on the GPU -> + rel_bias[h][clamp(d, -R, R) + R].
     """
     alibi_slopes: torch.Tensor | None = None
     symmetric: bool = False
     rel_bias: torch.Tensor | None = None
+    softcap: float | None = None
 
     def desc(self) -> attn_score_mod:
         d = attn_score_mod()
         d.flags = 0
         d.slopes = d.rel_bias = None
         d.rel_radius = 0
+        d.softcap = 0.0
+        if self.softcap is not None:
+            d.flags |= SCORE_SOFTCAP
+            d.softcap = float(self.softcap)
         if self.alibi_slopes is not None:
             t = self.alibi_slopes
             if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():

@@ -70,9 +70,9 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
 // work group stages.  `prefill_d64`: the prefill and backward kernels at
 // D = 64 are not offered with a score change (their score-change variants
 // are switched off after a GPU memory fault whose cause is not yet found).
-int make_smod(const attn_score_mod* m, bool allow_rel, int G_bwd, bool prefill_d64,
+int make_smod(const attn_score_mod* m, float scale, bool allow_rel, int G_bwd, bool prefill_d64,
               ScoreParams& out) {
-  out = ScoreParams{0u, nullptr, nullptr, 0};
+  out = ScoreParams{0u, nullptr, nullptr, 0, 0.f, 0.f};
   if (m == nullptr || m->flags == 0) return ATTN_OK;
   const uint32_t f = m->flags;
   if (prefill_d64) return ATTN_ERR_SCORE_MOD;
@@ -84,6 +84,11 @@ int make_smod(const attn_score_mod* m, bool allow_rel, int G_bwd, bool prefill_d
     if (m->rel_bias == nullptr) return ATTN_ERR_NULL;
     if (m->rel_radius < 0 || 2 * m->rel_radius + 1 > kMaxRelTable) return ATTN_ERR_SCORE_MOD;
     if (G_bwd > 0 && (int64_t)G_bwd * (2 * m->rel_radius + 1) > 8192) return ATTN_ERR_SCORE_MOD;
+  }
+  if (f & ATTN_SCORE_SOFTCAP) {
+    if (!(std::isfinite(m->softcap) && m->softcap > 0.f)) return ATTN_ERR_SCORE_MOD;
+    out.cap_in = scale / m->softcap;
+    out.cap_out = m->softcap * 1.4426950408889634f;
   }
   out.flags = f;
   out.slopes = m->slopes;
@@ -187,7 +192,7 @@ AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_sco
 
 extern "C" {
 
-int attn_abi_version(void) { return 5; }
+int attn_abi_version(void) { return 6; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -218,7 +223,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if (st) return st;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
-  if ((st = make_smod(smod, true, 0, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
@@ -271,7 +276,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
-  if ((st = make_smod(smod, true, 0, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   p.part_num = bm->part_num; p.part_idx = bm->part_idx;
@@ -334,7 +339,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
-  if ((st = make_smod(smod, false, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, false, 0, false, p.smod))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
   p.q = q;
@@ -407,7 +412,7 @@ int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
                     D, dtype, scale, mask, smod, stream);
   DecParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
-  if ((st = make_smod(smod, false, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, false, 0, false, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (workspace == nullptr) return ATTN_ERR_NULL;
   if (workspace_bytes < pl.ws_bytes) return ATTN_ERR_WORKSPACE;
@@ -474,7 +479,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if ((st = check_scale(scale))) return st;
   BwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
-  if ((st = make_smod(smod, true, Hq / Hkv, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, true, Hq / Hkv, D == 64, p.smod))) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   p.q = q;

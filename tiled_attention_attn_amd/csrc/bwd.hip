@@ -316,12 +316,15 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
           if (base + off > width) sacc[blk][r] = kNegInf;
         }
     }
+    // tanh of the capped scores (SOFTCAP only): dS takes the factor 1 - tanh^2
+    f32x16 th[NQB];
     if constexpr (SM) {
-      // scores now carry c2 and the bias of query head kvh G + g
+      // scores now carry c2 (or the cap) and the bias of query head kvh G + g
       const ScoreHead hd{alibi_slope2(p.smod, kvh * p.G + g), tabs + g * (2 * p.smod.R + 1)};
       const int d0 = key - (int)(q0 + 4 * half + shift);
-      add_score_bias<NQB, 16>(sacc, p.c2, p.smod, hd,
-                              [&](int blk, int r) { return d0 - (32 * blk + 8 * (r >> 2) + (r & 3)); });
+      add_score_bias<NQB, 16, true>(
+          sacc, p.c2, p.smod, hd,
+          [&](int blk, int r) { return d0 - (32 * blk + 8 * (r >> 2) + (r & 3)); }, th);
     }
 #pragma unroll
     for (int blk = 0; blk < NQB; ++blk) {
@@ -338,6 +341,12 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
       for (int r = 0; r < 16; ++r) {
         pr[r] = fast_exp2(__builtin_fmaf(sacc[blk][r], SM ? 1.f : p.c2, -l2[r >> 2][r & 3]));
         ds[r] = pr[r] * (dpacc[blk][r] - dl[r >> 2][r & 3]);
+      }
+      if constexpr (SM) {
+        if (p.smod.flags & ATTN_SCORE_SOFTCAP) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] *= __builtin_fmaf(-th[blk][r], th[blk][r], 1.f);
+        }
       }
       vec8<T> pp[2], pd[2];
 #pragma unroll
@@ -571,15 +580,22 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
           if (base_ok + off > width) sacc[r] = kNegInf;
         }
       }
+      f32x16 th;  // tanh of the capped scores (SOFTCAP only)
       if constexpr (SM) {
         const int d0 = kb + 32 * kbk + 4 * half - (int)(qrow + shift);
-        add_score_bias<1, 16>(&sacc, p.c2, p.smod, hd,
-                              [&](int, int r) { return d0 + 8 * (r >> 2) + (r & 3); });
+        add_score_bias<1, 16, true>(
+            &sacc, p.c2, p.smod, hd, [&](int, int r) { return d0 + 8 * (r >> 2) + (r & 3); }, &th);
       }
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         ds[r] = fast_exp2(__builtin_fmaf(sacc[r], SM ? 1.f : p.c2, -l2)) * (dpacc[r] - dl);
+      if constexpr (SM) {
+        if (p.smod.flags & ATTN_SCORE_SOFTCAP) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] *= __builtin_fmaf(-th[r], th[r], 1.f);
+        }
+      }
       // ---- dQ^T += K^T dS^T over these 32 keys (two 16-key chunks) ----
 #pragma unroll
       for (int c = 0; c < 2; ++c) {

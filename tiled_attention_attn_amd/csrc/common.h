@@ -241,15 +241,19 @@ __device__ __forceinline__ void row_interval(const MaskParams& m, int b, int64_t
 }
 
 // ---- score_mod ---------------------------------------------------------------
-// Additive changes of the scaled score before the softmax: ALiBi, symmetric
-// ALiBi, and a relative-position bias table (flags of attn_score_mod).  The
-// kernels work in base-2 units, so a score becomes s c2 + log2(e) bias(d)
-// with d = key - query position.
+// Changes of the scaled score before the softmax (flags of attn_score_mod):
+// tanh capping, then the additive ALiBi, symmetric ALiBi and relative-position
+// bias table.  The kernels work in base-2 units, so a raw dot product x
+// becomes x c2 + log2(e) bias(d), or with the cap
+// cap log2(e) tanh(x scale / cap) + log2(e) bias(d), with d = key - query
+// position.
 struct ScoreParams {
   uint32_t flags;
   const float* slopes;  // [Hq]
   const float* rel;     // [Hq][2R+1]
   int32_t R;
+  float cap_in;   // scale / cap
+  float cap_out;  // cap * log2(e)
 };
 
 // Largest relative-bias table a kernel stages in LDS for one head (floats).
@@ -275,16 +279,38 @@ __device__ __forceinline__ float alibi_slope2(const ScoreParams& sp, int h) {
   return (sp.flags & (ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM)) ? sp.slopes[h] * kLog2e : 0.f;
 }
 
+// tanh(u) = sign(u) (1 - 2 / (e^{2|u|} + 1)): one exp2 and one reciprocal;
+// +-1 exactly once e^{2|u|} overflows, absolute error a few 2^-24 near 0.
+__device__ __forceinline__ float cap_tanh(float u) {
+  const float e = fast_exp2((2.f * kLog2e) * __builtin_fabsf(u));
+  return __builtin_copysignf(1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f), u);
+}
+
 // acc[i][r] = acc[i][r] * c2 + log2(e) bias(dist(i, r)) over NB accumulators of
-// NE elements; -inf (masked) stays -inf.  One loop per term behind uniform
-// branches, so no per-element branching.
-template <int NB, int NE, typename V, typename DistFn>
+// NE elements, the first term capped as cap log2(e) tanh(acc scale / cap) with
+// SOFTCAP (the tanh goes to th[i][r] when KEEP_T, for the backward pass's
+// factor 1 - tanh^2); -inf (masked) stays -inf.  One loop per term behind
+// uniform branches, so no per-element branching.
+template <int NB, int NE, bool KEEP_T = false, typename V, typename DistFn>
 __device__ __forceinline__ void add_score_bias(V* acc, float c2, const ScoreParams& sp,
-                                               const ScoreHead& hd, DistFn dist) {
+                                               const ScoreHead& hd, DistFn dist,
+                                               V* th = nullptr) {
+  if (sp.flags & ATTN_SCORE_SOFTCAP) {
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int r = 0; r < NE; ++r) acc[i][r] *= c2;
+      for (int r = 0; r < NE; ++r) {
+        const float x = acc[i][r];
+        const float t = cap_tanh(sp.cap_in * x);
+        if constexpr (KEEP_T) th[i][r] = t;
+        acc[i][r] = x == kNegInf ? kNegInf : sp.cap_out * t;
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int r = 0; r < NE; ++r) acc[i][r] *= c2;
+  }
   if (sp.flags & ATTN_SCORE_ALIBI) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)

@@ -121,10 +121,11 @@ decode_kernel(const DecParams p) {
     whi = min(whi, __shfl_xor(whi, m, 64));
   }
 
-  // Score change (SM): ALiBi only here (the host rejects a bias table); the
-  // lane's query head hq sets its slope.  Scores then carry c2 and the bias.
+  // Score change (SM): ALiBi and the cap only here (the host rejects a bias
+  // table); the lane's query head hq sets its slope.  Scores then carry c2
+  // (or the cap) and the bias.
   ScoreParams sp = p.smod;
-  sp.flags &= ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM;
+  sp.flags &= ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM | ATTN_SCORE_SOFTCAP;
   ScoreHead hd{0.f, nullptr};
   if constexpr (SM) hd.slope2 = alibi_slope2(sp, hq);
   const float c2e = SM ? 1.f : p.c2;
