@@ -111,7 +111,10 @@ def bench_prefill_causal(T, W, steps, warmup):
     fn = lambda: T.attn_fwd(q, k, v, o, lse, wl.scale, desc)
     avg, best, wall = time_launches(fn, steps, warmup)
     flops = 4.0 * 64 * 2 * 16 * causal_pairs(4096)
-    return wl, dict(avg_ms=avg, min_ms=best, wall_ms=wall, flops=flops)
+    # Executed work: each 128-row query tile t runs t + 1 steps of 128 keys in full
+    # (the diagonal step's masked half included).
+    executed = 4.0 * 64 * 2 * 16 * sum((t + 1) * 128 * 128 for t in range(4096 // 128))
+    return wl, dict(avg_ms=avg, min_ms=best, wall_ms=wall, flops=flops, executed_flops=executed)
 
 
 def bench_prefill_others(T, W, steps, warmup):
@@ -353,7 +356,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("fwd_kernel<64,false>/causal_b2h16n4096d64"),
                      "traffic_unit": "bytes/launch", "kernel": "fwd_kernel<64, false, bf16, false>",
-                     "kernel_us": round(pf["avg_ms"] * 1e3, 2)},
+                     "kernel_us": round(pf["avg_ms"] * 1e3, 2),
+                     "useful_gflop": round(pf["flops"] / 1e9, 3),
+                     "executed_gflop": round(pf["executed_flops"] / 1e9, 3),
+                     "executed_tflops": round(pf["executed_flops"] / pf["avg_ms"] / 1e9, 2)},
     }
     if not args.quick and args.only == "all":
         dec = bench_decode(T, W, args.steps, args.warmup)
