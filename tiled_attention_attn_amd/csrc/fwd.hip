@@ -233,13 +233,25 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     // ---- S^T = K Q^T for the step's keys, in 32-key blocks ----
     f32x16 sacc[NKB];
 #pragma unroll
-    for (int kbk = 0; kbk < NKB; ++kbk) {
-      sacc[kbk] = f32x16{};
+    for (int kbk = 0; kbk < NKB; ++kbk) sacc[kbk] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk) {
         const vec8<T> kf = lds_read_b128<T>(tK, k_addr[c] + kbk * 32 * 2 * D);
         sacc[kbk] = mfma32(kf, qf[c], sacc[kbk]);
       }
+    }
+    // Keep the K operand reads about four MFMAs ahead of their use.
+    {
+      constexpr int NS = NKB * NC;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     // ---- mask (partial steps only) ----
     // Element (kbk, r) holds key kb + 32 kbk + 8 (r/4) + 4 half + r%4; it is
@@ -293,8 +305,14 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
       }
       return ps0 + ps1;
     };
-    float psum = probs(m_ref == kNegInf ? 0.f : m_ref);
-    if (__any((m_ref == kNegInf && sees) || !(psum <= kSumCap))) {
+    // A row that sees its first key needs the row max anyway: go straight to it.
+    float psum = 0.f;
+    bool fix = __any(m_ref == kNegInf && sees);
+    if (!fix) {
+      psum = probs(m_ref == kNegInf ? 0.f : m_ref);
+      fix = __any(!(psum <= kSumCap));
+    }
+    if (fix) {
       float mx = sacc[0][0];
 #pragma unroll
       for (int kbk = 0; kbk < NKB; ++kbk)
