@@ -52,6 +52,8 @@ SPLIT = [
     ("rows64_g64_d128", 1, 64, 1, 1, 600, 128, {"causal": True}, "bhnd"),
     ("ragged_d64", 3, 6, 3, 5, 777, 64, {"causal": True, "window": (300, 0)}, "bhnd"),
     ("one_query_d128", 4, 8, 8, 1, 513, 128, {"causal": True}, "bnhd"),
+    ("min_keys_d64", 2, 4, 2, 3, 512, 64, {"causal": True}, "bhnd"),          # Nk at the threshold
+    ("single_split_d64", 64, 8, 8, 1, 700, 64, {"causal": True}, "bhnd"),     # B * Hkv = 512: S = 1
 ]
 
 
@@ -90,25 +92,28 @@ def test_split_path_key_counts(name):
     assert np.max(np.abs(f64(lse) - np.log(cnt))) <= COUNT_LSE_TOL
 
 
-def test_split_path_fp16_and_alibi():
-    """fp16 inputs and ALiBi (D = 64 and 128) on the split-KV path."""
-    from test_gpu_score_mod import alibi_slopes
-    for D, dtype, sym in ((128, torch.float16, False), (64, torch.bfloat16, True)):
-        announce(f"auto split D={D} {dtype} alibi sym={sym}")
+def test_split_path_fp16_alibi_softcap():
+    """fp16 inputs, ALiBi and the soft-cap (D = 64 and 128) on the split-KV path."""
+    from test_gpu_score_mod import alibi_slopes, CAP
+    for D, dtype, sym, cap in ((128, torch.float16, False, False), (64, torch.bfloat16, True, False),
+                               (128, torch.bfloat16, False, True)):
+        announce(f"auto split D={D} {dtype} alibi sym={sym} cap={cap}")
         B, Hq, Hkv, Nq, Nk = 2, 8, 2, 12, 2100
         g = W.generator(31 + D)
         q = W.randn_half(g, (B, Hq, Nq, D), dtype)
         k = W.randn_half(g, (B, Hkv, Nk, D), dtype)
         v = W.randn_half(g, (B, Hkv, Nk, D), dtype)
         slopes = alibi_slopes(Hq)
-        smod = T.ScoreMod(alibi_slopes=slopes.to(DEV), symmetric=sym)
+        smod = T.ScoreMod(alibi_slopes=slopes.to(DEV), symmetric=sym, softcap=CAP if cap else None)
         spec = {"window": (900, 900)} if sym else {"causal": True}
         gm, mod = _mask_pair(spec, B, Nq, Nk)
         o, lse = _auto(q, k, v, 1.0 / math.sqrt(D), gm, smod=smod, expect=T.PATH_SPLITKV)
         assert o.dtype == dtype
         sm = (SM.alibi_sym if sym else SM.alibi)(slopes.double().numpy(), Nq, Nk)
+        if cap:
+            sm = SM.combine(SM.softcap(CAP), sm)
         ro, rl = oracle.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), mod, score_mod=sm)
-        assert_close(f64(o), f64(lse), ro, rl, f"alibi D={D}")
+        assert_close(f64(o), f64(lse), ro, rl, f"alibi D={D} cap={cap}")
 
 
 def test_prefill_path_is_attn_fwd():
