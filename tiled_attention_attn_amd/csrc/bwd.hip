@@ -567,11 +567,18 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
       // ---- S^T = K Q^T and dP^T = V dO^T for 32 keys ----
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c) {
         sacc = mfma32(lds_read_b128<T>(tK, k_addr[c] + kbk * 32 * ROW_BYTES), qf[c], sacc);
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
         dpacc = mfma32(lds_read_b128<T>(tV, k_addr[c] + kbk * 32 * ROW_BYTES), df[c], dpacc);
+      }
+      // Keep the operand reads about four MFMAs ahead of their use.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NC - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // element r holds key kb + 32 kbk + 8 (r/4) + 4 half + r%4
       if (masked) {
 #pragma unroll
