@@ -259,8 +259,14 @@ __device__ __forceinline__ void pp_tile(const FwdParams& p, TATTN_LDS char* smem
     }
     // P against the row's reference; the reference moves (O and l rescaled)
     // only when a partial sum shows it stale or the row's first key arrives.
-    float psum = probs(m_ref == kNegInf ? 0.f : m_ref);
-    if (__any((m_ref == kNegInf && sees) || !(psum <= kPPSumCap))) {
+    // A row that sees its first key needs the row max anyway: go straight to it.
+    float psum = 0.f;
+    bool fix = __any(m_ref == kNegInf && sees);
+    if (!fix) {
+      psum = probs(m_ref == kNegInf ? 0.f : m_ref);
+      fix = __any(!(psum <= kPPSumCap));
+    }
+    if (fix) {
       float mx = sacc[0][0];
 #pragma unroll
       for (int kbk = 0; kbk < NKB; ++kbk)
