@@ -35,6 +35,9 @@
  *   where noted (then it is not written).
  * - D is 64 or 128.  Hq must be a multiple of Hkv (GQA, consecutive
  *   grouping: query head hq reads KV head hq / (Hq / Hkv)).
+ * - A call whose one-dimensional work-group count would pass 2^31 - 1
+ *   (B * Hq * ceil(Nq / 128) for the prefill and dQ kernels, B * Hkv *
+ *   ceil(Nk / 128) for dK/dV) fails with ATTN_ERR_SHAPE before any launch.
  * - scale must be finite and > 0 (callers wanting 1/sqrt(D) pass it).
  * - Every pointer to tensor data is a DEVICE pointer owned by the caller.
  *   The library allocates nothing, frees nothing, keeps no state between

@@ -188,6 +188,22 @@ def test_bwd_argument_errors(T):
                dk=None, dv=None) == 0
 
 
+def test_grids_beyond_the_launch_limit_are_rejected(T):
+    """Shapes whose work-group count passes 2^31 - 1 fail on the host (ATTN_ERR_SHAPE)
+    instead of launching a truncated grid."""
+    big = dict(B=65535, Hq=65535, Hkv=65535, Nq=1 << 20, Nk=256)
+    assert _fwd(T, **big) == -2
+    lib = T.lib_handle()
+    qs = _strides(64 * 256, 64 * 256, 64)
+    bm = T.attn_blockmask(Bm=1, Hm=1, nQt=(1 << 20) // 128, nKt=2, part_num=16, part_idx=32, full_num=48,
+                          full_idx=64)
+    assert lib.attn_fwd_blockmask(16, qs, 32, qs, 48, qs, 64, qs, None, 65535, 65535, 65535, 1 << 20, 256, 64,
+                                  0, 0.125, None, None, ctypes.byref(bm), None) == -2
+    assert lib.attn_bwd(16, qs, 32, qs, 48, qs, 64, qs, 80, qs, 96, 112, qs, 128, qs, 144, qs,
+                        65535, 65535, 65535, 1 << 20, 256, 64, 0, 0.125, None, None, 160, 1 << 62, None) == -2
+    # just inside the limit the same calls would launch, so they are not made here
+
+
 def test_auto_plan_rule(T):
     """attn_fwd_auto's choice: split-KV for G * Nq <= 64 rows per KV head and Nk >= 512
     (no relative-bias table); the split count targets 512 work groups with >= 256 keys each,

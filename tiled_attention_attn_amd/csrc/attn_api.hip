@@ -139,6 +139,11 @@ void fill_fwd(FwdParams& p, const void* q, const int64_t* qs, const void* k, con
   p.nKt = (Nk + 127) / 128;
 }
 
+// Work-group counts (and the (batch, head, tile) indices the kernels derive
+// from them in 32-bit arithmetic) must stay within a 1-D grid: at most
+// 2^31 - 1 groups.
+bool grid_fits(int64_t groups) { return groups <= 0x7fffffffLL; }
+
 bool causal_like(const MaskParams& m) {
   return (m.flags & (ATTN_MASK_CAUSAL | ATTN_MASK_BLOCK_CAUSAL)) != 0 &&
          !(m.flags & (ATTN_MASK_WINDOW | ATTN_MASK_DOCUMENT));
@@ -225,6 +230,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
   if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
+  if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   // Causal-like masks give later query tiles more keys: pair tile i with n-1-i.
   set_slots(p, causal_like(p.mask));
@@ -278,6 +284,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
   if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
+  if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
   p.part_num = bm->part_num; p.part_idx = bm->part_idx;
   p.full_num = bm->full_num; p.full_idx = bm->full_idx;
@@ -516,6 +523,10 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   p.q_paired = pair && p.n_qt > 1;
   p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
   p.q_xcd_remap = ((long)B * Hq * p.q_slots) % 8 == 0;
+  // dQ groups B Hq n_qt, dK/dV groups B Hkv n_kt, Delta threads 8 per padded row
+  if (!grid_fits((int64_t)B * Hq * p.n_qt) || !grid_fits((int64_t)B * Hkv * p.n_kt) ||
+      !grid_fits(((int64_t)B * Hq * p.nq_pad * 8 + 255) / 256))
+    return ATTN_ERR_SHAPE;
   return launch_bwd(p, D, dtype, stream);
 }
 
