@@ -287,7 +287,14 @@ def cpu_baseline(budget_s=12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), model)
+    except OSError:
+        pass
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), cpu_model=model,
+                seconds=round(dt, 2), kind="oracle",
                 sample=f"{heads} of 32 (batch, head) slices of causal_b2h16n4096d64, fp64 NumPy, "
                        f"{dt:.1f} s")
 

@@ -53,6 +53,7 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, what="", o_tol=O_TOL, lse_tol=L
         fin = ~ninf_r
         el = float(np.max(np.abs(lse_gpu[fin] - lse_ref[fin]))) if fin.any() else 0.0
         assert el <= lse_tol, f"{what}: max |LSE err| {el:.3e} > {lse_tol}"
+    print(f"[err] {what}: max |O err| {eo:.3e}, max |LSE err| {el:.3e}", flush=True)
     return eo, el
 
 
