@@ -88,9 +88,9 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     const T* src = Qbh + (int64_t)r * p.q_sn + 8 * half;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const vec8<T>*>(src + 16 * c);
-    // Complete these loads here, so the waits inside the step loop only ever
-    // concern the asynchronous K/V copies.
-    wait_vmem();
+    // No wait here: these loads stay in flight with the first K/V copies, and
+    // the first step's full vmcnt wait (or the compiler's own wait before a
+    // use) completes them.
   }
 
   int lo, hi;
