@@ -30,7 +30,7 @@ from test_gpu_prefill import _mask_pair
 
 pytestmark = pytest.mark.gpu
 
-if torch.cuda.is_available():  # the HIP library must load on a GPU machine: no fallback
+if torch.cuda.is_available():  # with a GPU present the HIP library must load: no fallback
     import tiled_attention_attn_amd as T
 DEV = "cuda"
 REL = 2.0 ** -7

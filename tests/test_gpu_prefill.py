@@ -14,7 +14,7 @@ from gpu_util import (O_TOL, LSE_TOL, COUNT_LSE_TOL, f64, LazyF64, assert_close,
 
 pytestmark = pytest.mark.gpu
 
-if torch.cuda.is_available():  # on a GPU machine the HIP library must load: no fallback
+if torch.cuda.is_available():  # with a GPU present the HIP library must load: no fallback
     import tiled_attention_attn_amd as T
 DEV = "cuda"
 

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 # and their GPU cases are skipped until one is.
 D64_OFF = "score changes at D=64 are switched off after an unexplained GPU fault"
 
-if torch.cuda.is_available():  # the HIP library must load on a GPU machine: no fallback
+if torch.cuda.is_available():  # with a GPU present the HIP library must load: no fallback
     import tiled_attention_attn_amd as T
 DEV = "cuda"
 
