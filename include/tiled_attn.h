@@ -126,9 +126,9 @@ typedef struct attn_mask_desc {
  * and treats the biases and the cap as constants (no gradient for them).
  * SOFTCAP needs a finite softcap > 0.
  * REL_BIAS needs 0 <= R <= 1023 and, in attn_bwd, (Hq / Hkv) * (2R + 1) <=
- * 8192; attn_decode_splitkv takes ALIBI / ALIBI_SYM / SOFTCAP only.  attn_fwd,
- * attn_fwd_blockmask and attn_bwd take a score change at D = 128 only
- * (ATTN_ERR_SCORE_MOD at D = 64).
+ * 8192.  attn_fwd, attn_fwd_blockmask and attn_bwd take a score change at
+ * D = 128 only (ATTN_ERR_SCORE_MOD at D = 64); attn_decode_splitkv takes
+ * every score change at D = 64 and 128.
  */
 #define ATTN_SCORE_ALIBI 1u
 #define ATTN_SCORE_ALIBI_SYM 2u
@@ -278,8 +278,8 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
  * attn_fwd, on contiguous (non-paged) K/V.
  *
  * The split-KV path is taken when all G * Nq query rows of a KV head fit one
- * 64-row group (G = Hq / Hkv, so G * Nq <= 64), Nk >= 512, and smod carries
- * no ATTN_SCORE_REL_BIAS.  It runs the split-KV kernel over K/V in place and
+ * 64-row group (G = Hq / Hkv, so G * Nq <= 64) and Nk >= 512.  It runs the
+ * split-KV kernel over K/V in place and
  * then the combine: K/V are read once per KV head rather than once per query
  * head, and the key splits fill the GPU.  Every other shape runs attn_fwd.
  *
@@ -291,8 +291,8 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
  * plan.workspace_bytes, 16-byte aligned, overwritten (fp32 partial O and LSE
  * of every split); it may be NULL when that is 0.  ATTN_ERR_WORKSPACE when
  * workspace_bytes is smaller.  On the split-KV path the mask menu is
- * attn_fwd's (DOCUMENT included) and smod may carry ALiBi at D = 64 and 128;
- * on the prefill path every attn_fwd rule holds.  Results match attn_fwd to
+ * attn_fwd's (DOCUMENT included) and smod may carry any score change at
+ * D = 64 and 128; on the prefill path every attn_fwd rule holds.  Results match attn_fwd to
  * rounding (a different order of the key sums), not bit for bit.
  */
 #define ATTN_PATH_PREFILL 0

@@ -132,7 +132,8 @@ def test_blockmask_and_decode_argument_errors(T):
     assert dec(bts=3) == -2
     assert dec(D=80) == -3
     assert dec(dt=5) == -12
-    assert dec(smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=2)) == -13  # no table in decode
+    assert dec(smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=1024)) == -13  # 2R + 1 > 2048
+    assert dec(smod=T.attn_score_mod(flags=4, rel_bias=None, rel_radius=2)) == -1
     assert dec(smod=T.attn_score_mod(flags=8, softcap=0.0)) == -13
     assert dec(Hq=3) == -4
     md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=1, doc_stride=2)
@@ -205,8 +206,8 @@ def test_grids_beyond_the_launch_limit_are_rejected(T):
 
 
 def test_auto_plan_rule(T):
-    """attn_fwd_auto's choice: split-KV for G * Nq <= 64 rows per KV head and Nk >= 512
-    (no relative-bias table); the split count targets 512 work groups with >= 256 keys each,
+    """attn_fwd_auto's choice: split-KV for G * Nq <= 64 rows per KV head and Nk >= 512;
+    the split count targets 512 work groups with >= 256 keys each,
     in whole 64-key steps; workspace = fp32 partial O (padded to 256 B) + partial LSE."""
     P = T.attn_fwd_auto_plan
     pl = P(16, 32, 8, 16, 32768, 128)
@@ -223,7 +224,7 @@ def test_auto_plan_rule(T):
     assert P(2, 16, 16, 4096, 4096, 64).path == T.PATH_PREFILL
     assert P(1, 8, 8, 0, 4096, 64).path == T.PATH_PREFILL
     rel = T.attn_score_mod(flags=T.SCORE_REL_BIAS, rel_bias=16, rel_radius=4)
-    assert P(16, 32, 8, 16, 32768, 128, rel).path == T.PATH_PREFILL
+    assert P(16, 32, 8, 16, 32768, 128, rel).path == T.PATH_SPLITKV   # every score change runs on both
     ali = T.attn_score_mod(flags=T.SCORE_ALIBI, slopes=16)
     assert P(16, 32, 8, 16, 32768, 128, ali).path == T.PATH_SPLITKV
     for B, Hq, Hkv, Nq, Nk in [(3, 12, 4, 5, 700), (1, 2, 1, 32, 99999), (7, 8, 2, 16, 4097)]:

@@ -116,17 +116,36 @@ def test_split_path_fp16_alibi_softcap():
         assert_close(f64(o), f64(lse), ro, rl, f"alibi D={D} cap={cap}")
 
 
+def test_split_path_bias_table():
+    """A relative-position bias table (with ALiBi) on the split-KV path, against the oracle."""
+    from test_gpu_score_mod import alibi_slopes
+    B, Hq, Hkv, Nq, Nk, D, R = 2, 8, 2, 12, 1800, 128, 40
+    announce("auto split bias table")
+    g = W.generator(91)
+    q = W.randn_bf16(g, (B, Hq, Nq, D))
+    k = W.randn_bf16(g, (B, Hkv, Nk, D))
+    v = W.randn_bf16(g, (B, Hkv, Nk, D))
+    slopes = alibi_slopes(Hq)
+    table = (0.5 * torch.randn(Hq, 2 * R + 1, generator=torch.Generator().manual_seed(3))).float()
+    smod = T.ScoreMod(alibi_slopes=slopes.to(DEV), rel_bias=table.to(DEV))
+    gm, mod = _mask_pair({"causal": True}, B, Nq, Nk)
+    o, lse = _auto(q, k, v, 1.0 / math.sqrt(D), gm, smod=smod, expect=T.PATH_SPLITKV)
+    sm = SM.combine(SM.alibi(slopes.double().numpy(), Nq, Nk), SM.rel_bias(table.double().numpy(), R, Nq, Nk))
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), 1.0 / math.sqrt(D), mod, score_mod=sm)
+    assert_close(f64(o), f64(lse), ro, rl, "auto split bias table")
+
+
 def test_prefill_path_is_attn_fwd():
-    """A prefill-shaped call (and a decode shape carrying a bias table) runs attn_fwd itself:
-    bitwise the same O and LSE."""
-    for (B, Hq, Hkv, Nq, Nk, D) in ((1, 4, 2, 300, 300, 64), (2, 4, 1, 16, 900, 128)):
+    """Prefill-shaped calls (80 query rows a KV head: too many for one split-KV group; one with
+    a bias table) run attn_fwd itself: bitwise the same O and LSE."""
+    for (B, Hq, Hkv, Nq, Nk, D) in ((1, 4, 2, 300, 300, 64), (2, 4, 1, 20, 900, 128)):
         announce(f"auto prefill {B}x{Hq}x{Hkv} {Nq}x{Nk} D={D}")
         g = W.generator(Nq + D)
         q = W.randn_bf16(g, (B, Hq, Nq, D)).to(DEV)
         k = W.randn_bf16(g, (B, Hkv, Nk, D)).to(DEV)
         v = W.randn_bf16(g, (B, Hkv, Nk, D)).to(DEV)
         smod = None
-        if Nq < 64:  # a relative-position table keeps a decode shape on the prefill kernels
+        if D == 128:
             tb = (0.3 * torch.randn(Hq, 9, generator=torch.Generator().manual_seed(1))).float().to(DEV)
             smod = T.ScoreMod(rel_bias=tb)
         assert T.attn_fwd_auto_plan(B, Hq, Hkv, Nq, Nk, D, smod).path == T.PATH_PREFILL

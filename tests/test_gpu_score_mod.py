@@ -190,6 +190,10 @@ DECODE = [
     ("alibi_d64_gqa8", 1, 8, 1, 4, 333, 64, [333], 5, None, "alibi"),
     ("cap_causal", 2, 8, 2, 5, 300, 128, [300, 171], 3, None, "cap"),
     ("cap_alibi_d64_gqa8", 1, 8, 1, 4, 333, 64, [333], 5, None, "cap+alibi"),
+    # bias tables: steps more than R = 32 keys before the drafts add the clamped end value,
+    # the others look the table up per element
+    ("rel_causal", 2, 8, 2, 5, 300, 128, [300, 171], 3, None, "rel"),
+    ("cap_alibi_sym_rel_window_d64", 1, 8, 1, 4, 700, 64, [700], 5, (100, 100), "cap+alibi_sym+rel"),
 ]
 
 
@@ -205,6 +209,10 @@ def test_decode_score_mod(case):
     kw = {"softcap": CAP} if "cap" in kind else {}
     if "alibi" in kind:
         kw.update(alibi_slopes=slopes.to(DEV), symmetric="sym" in kind)
+    R = 32
+    table = (0.5 * torch.randn(Hq, 2 * R + 1, generator=torch.Generator().manual_seed(len(name)))).float()
+    if "rel" in kind:
+        kw["rel_bias"] = table.to(DEV)
     sg = T.ScoreMod(**kw)
     ws_o = torch.empty(B, Hq, Lq, S, D, dtype=torch.float32, device=DEV)
     ws_l = torch.empty(B, Hq, Lq, S, dtype=torch.float32, device=DEV)
@@ -223,6 +231,8 @@ def test_decode_score_mod(case):
         mods = [SM.softcap(CAP)] if "cap" in kind else []
         if "alibi" in kind:
             mods.append((SM.alibi_sym if "sym" in kind else SM.alibi)(slopes.double().numpy(), Lq, sl[b]))
+        if "rel" in kind:
+            mods.append(SM.rel_bias(table.double().numpy(), R, Lq, sl[b]))
         smod = SM.combine(*mods)
         ro, rl = oracle.attention(f64(t["q"])[b:b + 1], kl, vl, wl.scale, mod, score_mod=smod)
         assert_close(f64(o[b:b + 1]), f64(lse[b:b + 1]), ro, rl, f"{name} b{b}")

@@ -160,8 +160,7 @@ void set_slots(FwdParams& p, bool paired) {
 // query rows of a KV head fit one 64-row group of the split-KV kernel, and
 // there are at least kAutoMinKeys keys -- runs split-KV + combine: K/V are
 // read once per KV head instead of once per query head, and the key splits
-// fill the GPU even when B * Hkv cannot.  A relative-position bias table
-// (not offered by the split-KV kernel) keeps the call on the prefill kernels.
+// fill the GPU even when B * Hkv cannot.
 constexpr int kAutoMinKeys = 512;
 constexpr int kAutoSplitKeys = 256;  // fewest keys per split
 constexpr long kAutoTargetGroups = 2L * 256;  // two work groups per CU on 256 CUs
@@ -172,10 +171,10 @@ struct AutoPlan {
 };
 
 AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_score_mod* smod) {
+  (void)smod;  // every score change runs on both paths
   AutoPlan pl{ATTN_PATH_PREFILL, 0, 0, 0, 0};
   const long rows = (long)(Hq / Hkv) * Nq;
-  const bool rel = smod != nullptr && (smod->flags & ATTN_SCORE_REL_BIAS) != 0;
-  if (Nq < 1 || rows > 64 || Nk < kAutoMinKeys || rel) return pl;
+  if (Nq < 1 || rows > 64 || Nk < kAutoMinKeys) return pl;
   const long units = (long)B * Hkv;
   long S = units > 0 ? (kAutoTargetGroups + units - 1) / units : 1;
   const long max_s = Nk / kAutoSplitKeys;
@@ -197,7 +196,7 @@ AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_sco
 
 extern "C" {
 
-int attn_abi_version(void) { return 6; }
+int attn_abi_version(void) { return 7; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -346,7 +345,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
-  if ((st = make_smod(smod, scale, false, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
   p.q = q;
@@ -419,7 +418,7 @@ int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
                     D, dtype, scale, mask, smod, stream);
   DecParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
-  if ((st = make_smod(smod, scale, false, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (workspace == nullptr) return ATTN_ERR_NULL;
   if (workspace_bytes < pl.ws_bytes) return ATTN_ERR_WORKSPACE;

@@ -121,14 +121,24 @@ decode_kernel(const DecParams p) {
     whi = min(whi, __shfl_xor(whi, m, 64));
   }
 
-  // Score change (SM): ALiBi and the cap only here (the host rejects a bias
-  // table); the lane's query head hq sets its slope.  Scores then carry c2
-  // (or the cap) and the bias.
+  // Score change (SM): the lane's query head hq sets its ALiBi slope and bias
+  // table row.  Scores then carry c2 (or the cap) and the bias.  The G bias
+  // tables of a work group do not fit beside the LDS ring, so the table term
+  // is added here from global memory: a step whose keys all lie more than R
+  // before every row's position adds the row's clamped end value rel_far
+  // (loaded once); only the steps within R of the query positions look the
+  // table up per element.
   ScoreParams sp = p.smod;
   sp.flags &= ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM | ATTN_SCORE_SOFTCAP;
   ScoreHead hd{0.f, nullptr};
   if constexpr (SM) hd.slope2 = alibi_slope2(sp, hq);
   const float c2e = SM ? 1.f : p.c2;
+  const bool rel = SM && (p.smod.flags & ATTN_SCORE_REL_BIAS) != 0;
+  const float* rel_row = p.smod.rel + (rel ? (int64_t)hq * (2 * p.smod.R + 1) : 0);
+  float rel_far = 0.f;
+  if (rel) rel_far = rel_row[0] * kLog2e;
+  // steps with kb + kDecKBlk - 1 < rel_near are far: every row sits at >= seq_len - Lq
+  const int64_t rel_near = (int64_t)seq_len - p.Lq - p.smod.R;
 
   // Q^T fragments (B operand, k = head dim, n = row).
   vec8<T> qf[NC];
@@ -220,6 +230,23 @@ decode_kernel(const DecParams p) {
       // element (kb16, r) holds key kb + 16 kb16 + 4 grp + r
       const int d0 = kb + 4 * grp - (int)pos;
       add_score_bias<NKB, 4>(sacc, p.c2, sp, hd, [&](int kb16, int r) { return d0 + 16 * kb16 + r; });
+      if (rel) {
+        if ((int64_t)kb + kDecKBlk - 1 < rel_near) {
+#pragma unroll
+          for (int kb16 = 0; kb16 < NKB; ++kb16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[kb16][r] += rel_far;
+        } else {
+          const int R = p.smod.R;
+#pragma unroll
+          for (int kb16 = 0; kb16 < NKB; ++kb16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int d = d0 + 16 * kb16 + r;
+              sacc[kb16][r] += rel_row[(d < -R ? -R : (d > R ? R : d)) + R] * kLog2e;
+            }
+        }
+      }
     }
     float mx = sacc[0][0];
 #pragma unroll
