@@ -146,6 +146,8 @@ def test_blockmask_and_decode_argument_errors(T):
     assert lib.attn_decode_num_splits(1, 1, 3, 256) == 3        # never more splits than pages
     assert lib.attn_decode_num_splits(1, 300, 10000, 256) == 5  # at most 2048 pages per split
     assert dec(S=1, maxp=4097, bts=4097) == -8                  # 4097 pages in one split
+    assert dec(Hq=65536 * 2, Hkv=2) == -2                       # Hq bounded like every entry point
+    assert dec(Hq=60000, Hkv=1, Lq=65536) == -2                 # G * Lq rows kept inside int
     assert lib.attn_decode_ws_o_bytes(16, 32, 16, 128, 4) == 16 * 32 * 16 * 4 * 128 * 4
 
 
@@ -278,3 +280,55 @@ def test_product_path_does_not_reach_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("Oracle", ""), f
                 assert "import workloads" not in src and "from workloads" not in src, f
+
+
+def test_binding_rejects_bad_tensors_before_any_call(T):
+    """The Python binding checks every tensor argument the C ABI cannot see (shapes the
+    kernels index with, one slope / table row per query head, a block-table row per
+    sequence, device placement) and raises before calling into the library.  CPU
+    tensors reach the shape checks first, then fail the device check."""
+    import torch
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.zeros(1, 4, 64, 64, **bf)
+    k = torch.zeros(1, 2, 64, 64, **bf)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(1, 4, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        T.attn_fwd(q, k, k, o, lse)                                # all on the CPU
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_fwd(q, k, torch.zeros(1, 2, 63, 64, **bf), o)      # v != k
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_fwd(q, k, k, torch.zeros(1, 4, 64, 128, **bf))      # o != q
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_fwd(q, k, k, o, torch.zeros(1, 4, 65))               # lse rows
+    with pytest.raises(TypeError, match="lse"):
+        T.attn_fwd(q, k, k, o, torch.zeros(1, 4, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        T.attn_fwd(q, k, k, o, lse, smod=T.ScoreMod(alibi_slopes=torch.zeros(3)))
+    with pytest.raises(ValueError, match="rel_bias"):
+        T.attn_fwd(q, k, k, o, lse, smod=T.ScoreMod(rel_bias=torch.zeros(2, 9)))
+    with pytest.raises(ValueError, match="doc_offsets"):
+        T.attn_fwd(q, k, k, o, lse, mask=T.Mask(doc_offsets=torch.zeros(2, 3, dtype=torch.int32)))
+    # backward: gradients shaped like their inputs, lse required
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_bwd(q, k, k, o, q, lse, q, torch.zeros(1, 4, 64, 64, **bf), k)
+    with pytest.raises(TypeError, match="lse"):
+        T.attn_bwd(q, k, k, o, q, None, q, k, k)
+    # decode: block table and seq_lens cover every sequence
+    qd = torch.zeros(3, 4, 2, 64, **bf)
+    pool = torch.zeros(10, 16, 2, 64, **bf)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    sl = torch.zeros(3, dtype=torch.int32)
+    ws_o, ws_l = torch.zeros(3, 4, 2, 2, 64), torch.zeros(3, 4, 2, 2)
+    with pytest.raises(ValueError, match="block_table"):
+        T.attn_decode_splitkv(qd, pool, pool, bt, sl, 4, 2, ws_o, ws_l)
+    with pytest.raises(ValueError, match="seq_lens"):
+        T.attn_decode_splitkv(qd, pool, pool, torch.zeros(3, 4, dtype=torch.int32), sl[:2], 4, 2,
+                              ws_o, ws_l)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        T.attn_decode_splitkv(qd, pool, pool, torch.zeros(3, 4, dtype=torch.int32), sl, 4, 2,
+                              ws_o, ws_l)
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_decode_combine(ws_o, ws_l, torch.zeros(3, 4, 2, 128, **bf))
+    with pytest.raises(ValueError, match="shape"):
+        T.attn_decode_combine(ws_o, torch.zeros(3, 4, 2, 3), torch.zeros(3, 4, 2, 64, **bf))

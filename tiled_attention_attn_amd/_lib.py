@@ -162,6 +162,76 @@ def _half(*ts):
     return _DTYPES[dt]
 
 
+def _shape(name, t, want):
+    """``t`` must have exactly shape ``want``."""
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _on_device(*named):
+    """Every (name, tensor) pair with a tensor must live on the GPU, on one device.  Checked
+    after the shapes, so a shape error is reported first wherever it can be seen."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
+def _check_lse(lse, B, H, N):
+    if lse is None:
+        return
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    _shape("lse", lse, (B, H, N))
+
+
+def _check_qkvo(q, k, v, o):
+    """Shapes of a prefill call: q/o [B,Hq,Nq,D], k/v [B,Hkv,Nk,D]; returns B, Hq, Hkv, Nq, Nk, D."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-d [B, H, N, D] tensor")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _shape("k", k, (B, Hkv, Nk, D))
+    _shape("v", v, (B, Hkv, Nk, D))
+    _shape("o", o, (B, Hq, Nq, D))
+    return B, Hq, Hkv, Nq, Nk, D
+
+
+def _mask_tensors(mask, B):
+    """The device tensors a Mask brings (doc_offsets must have one row per batch row)."""
+    if isinstance(mask, Mask) and mask.doc_offsets is not None:
+        if mask.doc_offsets.dim() != 2 or mask.doc_offsets.shape[0] != B:
+            raise ValueError(f"doc_offsets must have one row per batch row ({B}), "
+                             f"got shape {tuple(mask.doc_offsets.shape)}")
+        return [("doc_offsets", mask.doc_offsets)]
+    return []
+
+
+def _smod_tensors(smod, Hq):
+    """The device tensors a ScoreMod brings (one slope / one table row per query head)."""
+    if not isinstance(smod, ScoreMod):
+        return []
+    out = []
+    if smod.alibi_slopes is not None:
+        if smod.alibi_slopes.numel() < Hq:
+            raise ValueError(f"alibi_slopes needs {Hq} entries (one per query head), "
+                             f"got {smod.alibi_slopes.numel()}")
+        out.append(("alibi_slopes", smod.alibi_slopes))
+    if smod.rel_bias is not None:
+        if smod.rel_bias.dim() != 2 or smod.rel_bias.shape[0] < Hq:
+            raise ValueError(f"rel_bias needs {Hq} rows (one per query head), "
+                             f"got shape {tuple(smod.rel_bias.shape)}")
+        out.append(("rel_bias", smod.rel_bias))
+    return out
+
+
 @dataclass
 class Mask:
     """The mask menu of attn_mask_desc (AND-composed).
@@ -258,8 +328,10 @@ def attn_fwd(q, k, v, o, lse=None, scale=None, mask=None, stream=None, smod=None
     """O (and LSE) for q [B,Hq,Nq,D], k/v [B,Hkv,Nk,D] bf16 or fp16 CUDA tensors (any B/H/N
     strides)."""
     dt = _half(q, k, v, o)
-    B, Hq, Nq, D = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Nq, Nk, D = _check_qkvo(q, k, v, o)
+    _check_lse(lse, B, Hq, Nq)
+    _on_device(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), *_mask_tensors(mask, B),
+               *_smod_tensors(smod, Hq))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     keep_s, sp = _smod_ptr(smod)
@@ -299,6 +371,13 @@ def attn_build_blockmask(bm: BlockMask, B, Nq, Nk, mask=None, tile_map=None, str
     """Fill ``bm`` from a uint8 tile map [Bm, Hm, nQt, nKt] (CUDA) or from ``mask``."""
     if tile_map is not None and (tile_map.dtype != torch.uint8 or not tile_map.is_contiguous()):
         raise TypeError("tile_map must be a contiguous uint8 tensor")
+    if tile_map is not None:
+        _shape("tile_map", tile_map, (bm.Bm, bm.Hm, bm.nQt, bm.nKt))
+    if (bm.nQt, bm.nKt) != ((Nq + BLOCKMASK_TILE - 1) // BLOCKMASK_TILE,
+                            (Nk + BLOCKMASK_TILE - 1) // BLOCKMASK_TILE):
+        raise ValueError("BlockMask tile counts do not match Nq / Nk")
+    _on_device(("tile_map", tile_map), ("part_num", bm.part_num), ("part_idx", bm.part_idx),
+               ("full_num", bm.full_num), ("full_idx", bm.full_idx), *_mask_tensors(mask, B))
     keep, mp = _mask_ptr(mask)
     s = bm.struct()
     st = _lib.attn_build_blockmask(mp, _ptr(tile_map), B, Nq, Nk, ctypes.byref(s), _stream(stream))
@@ -309,8 +388,11 @@ def attn_build_blockmask(bm: BlockMask, B, Nq, Nk, mask=None, tile_map=None, str
 def attn_fwd_blockmask(q, k, v, o, bm: BlockMask, lse=None, scale=None, mask=None, stream=None,
                        smod=None):
     dt = _half(q, k, v, o)
-    B, Hq, Nq, D = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Nq, Nk, D = _check_qkvo(q, k, v, o)
+    _check_lse(lse, B, Hq, Nq)
+    _on_device(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("part_num", bm.part_num),
+               ("part_idx", bm.part_idx), ("full_num", bm.full_num), ("full_idx", bm.full_idx),
+               *_mask_tensors(mask, B), *_smod_tensors(smod, Hq))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     keep_s, sp = _smod_ptr(smod)
@@ -354,13 +436,25 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, n
         raise TypeError("seq_lens must be contiguous int32")
     if ws_o.dtype != torch.float32 or ws_lse.dtype != torch.float32:
         raise TypeError("workspaces must be float32")
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q and the caches must be 4-d, block_table 2-d")
     B, Hq, Lq, D = q.shape
     n_pages, page_size, Hkv, Dk = k_cache.shape
     if Dk != D:
         raise ValueError("head dim mismatch")
+    if block_table.shape[0] < B or block_table.shape[1] < max_pages:
+        raise ValueError(f"block_table must be at least [{B}, {max_pages}], "
+                         f"got {tuple(block_table.shape)}")
+    if seq_lens.numel() < B:
+        raise ValueError(f"seq_lens needs {B} entries, got {seq_lens.numel()}")
     if ws_o.numel() * 4 < attn_decode_ws_o_bytes(B, Hq, Lq, D, num_splits) or \
             ws_lse.numel() * 4 < attn_decode_ws_lse_bytes(B, Hq, Lq, num_splits):
         raise ValueError("workspace too small")
+    if not (ws_o.is_contiguous() and ws_lse.is_contiguous()):
+        raise TypeError("workspaces must be contiguous")
+    _on_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+               ("seq_lens", seq_lens), ("ws_o", ws_o), ("ws_lse", ws_lse),
+               *_smod_tensors(smod, Hq))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     keep_s, sp = _smod_ptr(smod)
@@ -375,9 +469,18 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seq_lens, max_pages, n
 def attn_decode_combine(ws_o, ws_lse, o, lse=None, stream=None):
     """O [B,Hq,Lq,D] bf16 / fp16 (and LSE [B,Hq,Lq]) from ws_o [B,Hq,Lq,S,D], ws_lse [B,Hq,Lq,S]."""
     dt = _half(o)
+    if ws_o.dim() != 5:
+        raise ValueError("ws_o must be a 5-d [B, Hq, Lq, S, D] tensor")
     B, Hq, Lq, S, D = ws_o.shape
-    if ws_o.dtype != torch.float32 or not ws_o.is_contiguous() or not ws_lse.is_contiguous():
+    if ws_o.dtype != torch.float32 or ws_lse.dtype != torch.float32 or not ws_o.is_contiguous() \
+            or not ws_lse.is_contiguous():
         raise TypeError("workspaces must be contiguous float32")
+    _shape("ws_lse", ws_lse, (B, Hq, Lq, S))
+    if o.dim() != 4:
+        raise ValueError("o must be a 4-d [B, Hq, Lq, D] tensor")
+    _shape("o", o, (B, Hq, Lq, D))
+    _check_lse(lse, B, Hq, Lq)
+    _on_device(("ws_o", ws_o), ("ws_lse", ws_lse), ("o", o), ("lse", lse))
     st = _lib.attn_decode_combine(_ptr(ws_o), _ptr(ws_lse), B, Hq, Lq, S, D, dt, _ptr(o),
                                   _strides(o), _ptr(lse), _stream(stream))
     _check("attn_decode_combine", st)
@@ -394,10 +497,16 @@ def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=
     and the forward pass's lse float [B,Hq,Nq]; ``workspace`` is a float32 CUDA tensor of at
     least attn_bwd_workspace_bytes(B, Hq, Nq) bytes (allocated here if None)."""
     dt = _half(q, k, v, o, d_o, dq, dk, dv)
-    B, Hq, Nq, D = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise TypeError("lse must be contiguous float32 [B, Hq, Nq]")
+    B, Hq, Hkv, Nq, Nk, D = _check_qkvo(q, k, v, o)
+    for name, t, want in (("d_o", d_o, q.shape), ("dq", dq, q.shape), ("dk", dk, k.shape),
+                          ("dv", dv, k.shape)):
+        _shape(name, t, want)
+    if lse is None:
+        raise TypeError("lse (the forward pass's float32 [B, Hq, Nq]) is required")
+    _check_lse(lse, B, Hq, Nq)
+    _on_device(("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o), ("lse", lse), ("dq", dq),
+               ("dk", dk), ("dv", dv), ("workspace", workspace), *_mask_tensors(mask, B),
+               *_smod_tensors(smod, Hq))
     need = attn_bwd_workspace_bytes(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
@@ -431,8 +540,10 @@ def attn_fwd_auto(q, k, v, o, lse=None, scale=None, mask=None, workspace=None, s
     ``workspace`` is a CUDA tensor of at least attn_fwd_auto_plan(...).workspace_bytes bytes
     (allocated here if None)."""
     dt = _half(q, k, v, o)
-    B, Hq, Nq, D = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Nq, Nk, D = _check_qkvo(q, k, v, o)
+    _check_lse(lse, B, Hq, Nq)
+    _on_device(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("workspace", workspace),
+               *_mask_tensors(mask, B), *_smod_tensors(smod, Hq))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     keep, mp = _mask_ptr(mask)
     keep_s, sp = _smod_ptr(smod)

@@ -330,7 +330,9 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   if (st) return st;
   if (B < 0 || Hq < 0 || Hkv < 0 || Lq < 0 || num_pages < 1 || page_size < 1 || max_pages < 1)
     return ATTN_ERR_SHAPE;
-  if (B > 65535 || Hkv > 65535 || Lq > 65536) return ATTN_ERR_SHAPE;
+  if (B > 65535 || Hq > 65535 || Hkv > 65535 || Lq > 65536) return ATTN_ERR_SHAPE;
+  // rows = G * Lq query rows per KV head stay well inside int
+  if ((int64_t)(Hkv > 0 ? Hq / Hkv : 0) * Lq > kMaxLen) return ATTN_ERR_SHAPE;
   if ((int64_t)max_pages * page_size > kMaxLen) return ATTN_ERR_SHAPE;
   if (bt_stride < max_pages) return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;

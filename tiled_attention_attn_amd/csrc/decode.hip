@@ -148,7 +148,12 @@ decode_kernel(const DecParams p) {
     for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const vec8<T>*>(src + 32 * c);
   }
   // The split's block-table entries go to LDS once, so the pipelined loop
-  // below issues no vector-memory loads other than the K/V copies.
+  // below issues no vector-memory loads other than the K/V copies -- except
+  // with a relative-position bias table: a step within R of the query
+  // positions reads its table entries from global memory, and the compiler's
+  // wait for those values (vmcnt counts in issue order) also drains the K/V
+  // copies just issued for later stages.  Only the last ceil((Lq + R) / 32)
+  // steps or so of the sequence are such steps.
   int page0 = 0, n_split_pages = 0;
   if constexpr (PAGED) {
     const int32_t* bt_row = p.bt + b * p.bt_stride;

@@ -40,7 +40,8 @@ constexpr int kQTile = 128;
 // per key; at D=128 the 128-key stage (64 KB) would not leave room for two.
 template <int D> struct KBlk { static constexpr int value = D == 64 ? 128 : 64; };
 constexpr int kThreads = 256;
-// A lane's partial row sum of P (32 values) above 2^12 moves the reference max.
+// A lane's partial row sum of P (64 values at D=64, 32 at D=128) above
+// kSumCap = 2^12 moves the reference max.
 constexpr float kSumCap = 4096.0f;
 
 // Pipeline depth: two 32 KB stages (K tile + V tile), so two work groups fit
@@ -281,13 +282,14 @@ __device__ __forceinline__ void process_tile(const FwdParams& p, TATTN_LDS char*
     // ---- online softmax against a lazily moved reference max ----
     // P = exp2(c2 s - m_ref) is taken against the row's reference m_ref
     // without a row max on the common path.  Every P value of a lane is at
-    // most that lane's partial row sum, so a partial sum <= 2^kSumCap proves
-    // them all in range.  Otherwise (a row max rose by about kSumCap, a
-    // non-finite score, or the first visible key of a row) the reference moves
-    // to the true row max, O and l are rescaled by exp2(m_old - m_new), and P
-    // is taken again.  Each row is thus normalised against some value at most
-    // kSumCap + log2(64) below its running max: the online softmax of
-    // section 3.2 with the rescale deferred until it is needed.
+    // most that lane's partial row sum, so a partial sum <= kSumCap = 2^12
+    // proves them all in range.  Otherwise (a row max rose by about
+    // log2(kSumCap) = 12 in base-2 units, a non-finite score, or the first
+    // visible key of a row) the reference moves to the true row max, O and l
+    // are rescaled by exp2(m_old - m_new), and P is taken again.  Each row is
+    // thus normalised against a reference at most 12 + log2(64) below its
+    // running max: the online softmax of section 3.2 with the rescale
+    // deferred until it is needed.
     vec8<T> pf[NKC];
     auto probs = [&](float m_use) -> float {
       float ps0 = 0.f, ps1 = 0.f;
