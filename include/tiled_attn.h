@@ -350,6 +350,18 @@ int attn_bwd(const void* q, const int64_t q_stride[3],
              const attn_mask_desc* mask, const attn_score_mod* smod,
              float* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- measurement helper -----------------------------------------------------
+ * attn_probe_stream_read: reads `bytes` of device memory at `src` once with a
+ * plain streaming kernel (16-byte loads, `blocks` work groups of 256 threads,
+ * grid-stride) and writes one 32-bit fold per work group to `sink` (device
+ * uint32 [blocks]).  No attention arithmetic: it gives the read rate a bare
+ * stream reaches on the device, the ceiling the decode kernel's KV-read rate
+ * is compared against.  src and bytes must be 16-byte aligned / a multiple of
+ * 16 (ATTN_ERR_ALIGN); 1 <= blocks <= 2^20 (ATTN_ERR_SHAPE).
+ */
+int attn_probe_stream_read(const void* src, size_t bytes, int blocks, uint32_t* sink,
+                           hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_str(int status);
 

@@ -109,6 +109,7 @@ def _load():
         "attn_bwd_workspace_bytes": (S, [I, I, I]),
         "attn_fwd_auto_plan": (I, [I, I, I, I, I, I, SP, ctypes.POINTER(attn_auto_plan)]),
         "attn_fwd_auto": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
+        "attn_probe_stream_read": (I, [P, S, I, P, P]),
         "attn_status_str": (ctypes.c_char_p, [I]),
         "attn_abi_version": (I, []),
     }
@@ -123,8 +124,8 @@ _lib = _load()
 EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_blockmask_bytes",
            "attn_decode_splitkv", "attn_decode_combine", "attn_decode_ws_o_bytes",
            "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_fwd_auto_plan", "attn_fwd_auto", "attn_status_str",
-           "attn_abi_version")
+           "attn_bwd_workspace_bytes", "attn_fwd_auto_plan", "attn_fwd_auto",
+           "attn_probe_stream_read", "attn_status_str", "attn_abi_version")
 
 
 def _check(func: str, status: int):
@@ -558,6 +559,19 @@ def attn_fwd_auto(q, k, v, o, lse=None, scale=None, mask=None, workspace=None, s
                             _stream(stream))
     _check("attn_fwd_auto", st)
     return o, lse
+
+
+def attn_probe_stream_read(src, sink, blocks=None, stream=None):
+    """Read all of ``src`` (a contiguous GPU tensor, size a multiple of 16 bytes) once with the
+    streaming probe kernel; ``sink`` is a GPU int32 tensor of at least ``blocks`` entries."""
+    if blocks is None:
+        blocks = sink.numel()
+    if not src.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < blocks:
+        raise ValueError("src must be contiguous and sink an int32 tensor of >= blocks entries")
+    _on_device(("src", src), ("sink", sink))
+    _check("attn_probe_stream_read",
+           _lib.attn_probe_stream_read(_ptr(src), src.numel() * src.element_size(), int(blocks),
+                                       _ptr(sink), _stream(stream)))
 
 
 def attn_status_str(status: int) -> str:
