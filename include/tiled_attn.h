@@ -42,7 +42,8 @@
  * - Every pointer to tensor data is a DEVICE pointer owned by the caller.
  *   The library allocates nothing, frees nothing, keeps no state between
  *   calls and never synchronises: each call validates its arguments on the
- *   host, then enqueues its kernels on `stream` and returns.
+ *   host, then enqueues its kernels on `stream` and returns.  The one
+ *   exception is attn_decode_noalloc's static per-GPU buffer (see there).
  * - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code.  Arguments are
  *   checked before any launch; on an error nothing is launched and no output
  *   is touched.  ATTN_ERR_LAUNCH reports hipGetLastError() after a launch.
@@ -261,6 +262,30 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse,
                         int B, int Hq, int Lq, int S, int D, int dtype,
                         void* o, const int64_t o_stride[3], float* lse,
                         hipStream_t stream);
+
+/* attn_decode_noalloc: attn_decode_splitkv followed by attn_decode_combine in
+ * one call that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments are attn_decode_splitkv's without ws_o /
+ * ws_lse, plus attn_decode_combine's outputs o / o_stride / lse; results are
+ * bit for bit those of the two calls with the same num_splits.
+ * The split partials live in a library-owned static device buffer of
+ * attn_decode_noalloc_max_bytes() = 32 MiB per GPU, held until the process
+ * ends: B * Hq * Lq * num_splits * (D + 1) * 4 bytes (plus alignment) must fit
+ * in it, else ATTN_ERR_WORKSPACE before any launch.  Every call on one GPU
+ * shares that GPU's buffer, so calls that overlap on one GPU (two streams, two
+ * host threads) race; calls ordered on one stream are safe.  The buffer's
+ * device address is looked up on a device's first call.
+ */
+int attn_decode_noalloc(const void* q, const int64_t q_stride[3],
+                        const void* k_cache, const void* v_cache, int64_t num_pages,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* seq_lens, int max_pages,
+                        int B, int Hq, int Hkv, int Lq, int D, int dtype, int page_size,
+                        int num_splits, float scale, const attn_mask_desc* mask,
+                        const attn_score_mod* smod, void* o, const int64_t o_stride[3],
+                        float* lse, hipStream_t stream);
+size_t attn_decode_noalloc_max_bytes(void);
 
 /* Workspace sizes of attn_decode_splitkv in bytes (0 on invalid sizes). */
 size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits);

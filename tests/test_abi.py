@@ -147,6 +147,23 @@ def test_blockmask_and_decode_argument_errors(T):
     assert lib.attn_decode_num_splits(1, 300, 10000, 256) == 5  # at most 2048 pages per split
     assert dec(S=1, maxp=4097, bts=4097) == -8                  # 4097 pages in one split
     assert dec(Hq=65536 * 2, Hkv=2) == -2                       # Hq bounded like every entry point
+    # the allocation-free variant: partials beyond its static buffer are refused before any launch
+    assert lib.attn_decode_noalloc_max_bytes() == 32 << 20
+
+    def dec_na(**kw):
+        a = args(**kw)
+        return lib.attn_decode_noalloc(a["q"], a["qs"], a["kc"], a["vc"], a["pages"], a["bt"], a["bts"],
+                                       a["sl"], a["maxp"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"],
+                                       a["dt"], a["ps"], a["S"], a["scale"], None, None, 128, qs, None,
+                                       None)
+    assert dec_na(B=16, Hq=32, Hkv=8, Lq=16, S=8) == -8    # 16*32*16*8*129*4 B > 32 MiB
+    assert dec_na(B=16, Hq=32, Hkv=8, Lq=16, S=65536) == -8
+    assert dec_na(S=0) == -8
+    assert dec_na(D=80) == -3
+    assert lib.attn_decode_noalloc(16, qs, 32, 48, 10, 64, 4, 80, 4, 1, 4, 2, 2, 128, 0, 16, 2, 0.1,
+                                   None, None, None, qs, None, None) == -1      # no output
+    assert lib.attn_decode_noalloc(16, qs, 32, 48, 10, 64, 4, 80, 4, 1, 4, 2, 2, 128, 0, 16, 2, 0.1,
+                                   None, None, 8, qs, None, None) == -6         # misaligned output
     assert dec(Hq=60000, Hkv=1, Lq=65536) == -2                 # G * Lq rows kept inside int
     assert lib.attn_decode_ws_o_bytes(16, 32, 16, 128, 4) == 16 * 32 * 16 * 4 * 128 * 4
 

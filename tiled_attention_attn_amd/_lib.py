@@ -101,6 +101,9 @@ def _load():
         "attn_blockmask_bytes": (S, [I, I, I, I]),
         "attn_decode_splitkv": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, I, F, MP, SP, P, P, P]),
         "attn_decode_combine": (I, [P, P, I, I, I, I, I, I, P, STR, P, P]),
+        "attn_decode_noalloc": (I, [P, STR, P, P, I64, P, I64, P, I, I, I, I, I, I, I, I, I, F, MP, SP,
+                                    P, STR, P, P]),
+        "attn_decode_noalloc_max_bytes": (S, []),
         "attn_decode_ws_o_bytes": (S, [I, I, I, I, I]),
         "attn_decode_ws_lse_bytes": (S, [I, I, I, I]),
         "attn_decode_num_splits": (I, [I, I, I, I]),
@@ -122,7 +125,8 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_blockmask_bytes",
-           "attn_decode_splitkv", "attn_decode_combine", "attn_decode_ws_o_bytes",
+           "attn_decode_splitkv", "attn_decode_combine", "attn_decode_noalloc",
+           "attn_decode_noalloc_max_bytes", "attn_decode_ws_o_bytes",
            "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_fwd_auto_plan", "attn_fwd_auto",
            "attn_probe_stream_read", "attn_status_str", "attn_abi_version")
@@ -485,6 +489,48 @@ def attn_decode_combine(ws_o, ws_lse, o, lse=None, stream=None):
     st = _lib.attn_decode_combine(_ptr(ws_o), _ptr(ws_lse), B, Hq, Lq, S, D, dt, _ptr(o),
                                   _strides(o), _ptr(lse), _stream(stream))
     _check("attn_decode_combine", st)
+    return o, lse
+
+
+def attn_decode_noalloc_max_bytes():
+    return int(_lib.attn_decode_noalloc_max_bytes())
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_pages, num_splits, o,
+                        lse=None, scale=None, mask=None, stream=None, smod=None):
+    """attn_decode_splitkv + attn_decode_combine in one call that allocates nothing (the split
+    partials live in the library's static per-GPU buffer); o [B,Hq,Lq,D], lse [B,Hq,Lq] or None."""
+    dt = _half(q, o)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("KV caches must have the dtype of q")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()) or k_cache.shape != v_cache.shape:
+        raise ValueError("KV caches must be contiguous [pages, page_size, Hkv, D] of one shape")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise TypeError("block_table must be int32 [B, >= max_pages] with contiguous rows")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise TypeError("seq_lens must be contiguous int32")
+    if q.dim() != 4 or k_cache.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, o and the caches must be 4-d")
+    B, Hq, Lq, D = q.shape
+    n_pages, page_size, Hkv, Dk = k_cache.shape
+    if Dk != D:
+        raise ValueError("head dim mismatch")
+    _shape("o", o, (B, Hq, Lq, D))
+    _check_lse(lse, B, Hq, Lq)
+    if block_table.shape[0] < B or block_table.shape[1] < max_pages:
+        raise ValueError(f"block_table must be at least [{B}, {max_pages}]")
+    if seq_lens.numel() < B:
+        raise ValueError(f"seq_lens needs {B} entries")
+    _on_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_table", block_table),
+               ("seq_lens", seq_lens), ("o", o), ("lse", lse), *_smod_tensors(smod, Hq))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
+    st = _lib.attn_decode_noalloc(_ptr(q), _strides(q), _ptr(k_cache), _ptr(v_cache), n_pages,
+                                  _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                                  int(max_pages), B, Hq, Hkv, Lq, D, dt, page_size, int(num_splits),
+                                  scale, mp, sp, _ptr(o), _strides(o), _ptr(lse), _stream(stream))
+    _check("attn_decode_noalloc", st)
     return o, lse
 
 
