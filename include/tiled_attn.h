@@ -95,8 +95,26 @@ extern "C" {
 #define ATTN_MASK_BLOCK_CAUSAL 8u /* k < block_size * (p / block_size + 1)        */
 #define ATTN_MASK_ALL 15u
 
+/* Schedule flags, carried in attn_mask_desc.flags beside the mask bits.  They
+ * change only which work group covers which tile and how the work groups are
+ * numbered on the GPU -- never a bit of any result, because every output row
+ * (and every dK / dV key) is produced by exactly one work group with a fixed
+ * order of its key (or row) sums.  They exist so a test can run one call
+ * under two schedules and require bitwise-equal outputs (a missing
+ * synchronisation would show up as a difference).
+ *   NO_PAIRING      causal-like masks: one query (key) tile per work group
+ *                   instead of the pair (i, n-1-i)
+ *   NO_XCD_REMAP    work groups numbered in launch order instead of whole
+ *                   heads per XCD
+ *   REVERSE         work groups numbered from the last to the first
+ */
+#define ATTN_SCHED_NO_PAIRING (1u << 16)
+#define ATTN_SCHED_NO_XCD_REMAP (1u << 17)
+#define ATTN_SCHED_REVERSE (1u << 18)
+#define ATTN_SCHED_ALL (7u << 16)
+
 typedef struct attn_mask_desc {
-  uint32_t flags;       /* ATTN_MASK_* bits                                        */
+  uint32_t flags;       /* ATTN_MASK_* bits (and optional ATTN_SCHED_* bits)       */
   int32_t window_left;  /* WINDOW: inclusive widths; a negative width leaves that  */
   int32_t window_right; /*   side unbounded.  Symmetric (w, w) is the pages' case. */
   int32_t block_size;   /* BLOCK_CAUSAL: block length (> 0)                        */

@@ -101,6 +101,14 @@ def test_fwd_argument_errors(T):
     assert _fwd(T, mask=m, Nq=300, Nk=256) == -7
 
 
+def test_schedule_flags_are_accepted_beside_the_mask(T):
+    m = T.attn_mask_desc(flags=T.MASK_CAUSAL | T.SCHED_ALL)
+    assert _fwd(T, Nq=0, mask=m) == 0                                # accepted, nothing to launch
+    assert _fwd(T, Nq=0, mask=T.attn_mask_desc(flags=1 << 20)) == -7
+    with pytest.raises(ValueError):
+        T.Mask(causal=True, schedule=1 << 20).desc()
+
+
 def test_empty_problems_launch_nothing(T):
     # B = 0 or Nq = 0: valid, nothing to do, returns OK without touching the GPU
     assert _fwd(T, B=0) == 0
@@ -201,6 +209,7 @@ def test_bwd_argument_errors(T):
     assert bwd(dv=150) == -6
     assert bwd(scale=-1.0) == -11
     assert bwd(mask=T.attn_mask_desc(flags=32)) == -7
+    assert bwd(mask=T.attn_mask_desc(flags=1 << 19)) == -7           # not a schedule bit either
     assert bwd(wsb=ws - 4) == -8
     assert bwd(B=0) == 0
     # no rows and no keys: nothing to compute; row-less tensors may be NULL

@@ -248,9 +248,9 @@ def test_fully_masked_rows():
     assert torch.all(o[0, 0, :50] == 0) and torch.all(torch.isneginf(lse[0, 0, :50]))
 
 
-def test_config2_causal_b2h16n4096d64_sampled_and_deterministic():
-    """Causal prefill B=2 H=16 N=4096 D=64 at full size: sampled rows vs the oracle, and
-    two runs bitwise equal."""
+def test_config2_causal_b2h16n4096d64_every_row_and_deterministic():
+    """Causal prefill B=2 H=16 N=4096 D=64 at full size: every (batch, head) and every row
+    against the oracle, element by element, and two runs bitwise equal."""
     announce("causal_b2h16n4096d64")
     wl = W.causal_b2h16n4096d64()
     q, k, v = (wl.tensors[x].to(DEV) for x in ("q", "k", "v"))
@@ -262,16 +262,13 @@ def test_config2_causal_b2h16n4096d64_sampled_and_deterministic():
     T.attn_fwd(q, k, v, o2, lse2, wl.scale, T.Mask(causal=True))
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
-    mod = M.causal(4096, 4096)
-    qa, ka, va = LazyF64(q), LazyF64(k), LazyF64(v)
-    for (b, h) in ((0, 0), (0, 7), (1, 15), (1, 3)):
-        rows = sample_rows(4096, 48, b * 16 + h)
-        ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, b, h, rows)
-        assert_close(f64(o[b, h, rows]), f64(lse[b, h, rows]), ro, rl, f"cfg2 b{b} h{h}")
+    ro, rl = oracle.attention(f64(wl.tensors["q"]), f64(wl.tensors["k"]), f64(wl.tensors["v"]),
+                              wl.scale, M.causal(4096, 4096), row_block=1024)
+    assert_close(f64(o), f64(lse), ro, rl, "cfg2 all 32 (b, h) x 4096 rows")
 
 
 @pytest.mark.parametrize("variant", ["window_doc", "blockdiff"])
-def test_config3_b1h32n8192d128_sampled(variant):
+def test_config3_b1h32n8192d128_every_head_sampled_rows(variant):
     name = "window_doc_b1h32n8192d128" if variant == "window_doc" else "blockdiff_b1h32n8192d128"
     announce(name)
     wl = W.FULL_SIZE[name]()
@@ -284,9 +281,9 @@ def test_config3_b1h32n8192d128_sampled(variant):
     lse = torch.empty(1, 32, 8192, dtype=torch.float32, device=DEV)
     T.attn_fwd(q, k, v, o, lse, wl.scale, gm)
     torch.cuda.synchronize()
-    qa, ka, va = LazyF64(q), LazyF64(k), LazyF64(v)
-    for h in (0, 13, 31):
-        rows = sample_rows(8192, 64, h)
+    qa, ka, va = (f64(wl.tensors[x]) for x in ("q", "k", "v"))
+    for h in range(32):
+        rows = sample_rows(8192, 48, h)
         ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, 0, h, rows)
         assert_close(f64(o[0, h, rows]), f64(lse[0, h, rows]), ro, rl, f"{name} h{h}")
 

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     AttnError, Mask, ScoreMod, BlockMask, LIB_PATH, EXPORTS, DTYPE_BF16, DTYPE_F16,
     SCORE_ALIBI, SCORE_ALIBI_SYM, SCORE_REL_BIAS, SCORE_SOFTCAP, attn_score_mod,
     MASK_CAUSAL, MASK_WINDOW, MASK_DOCUMENT, MASK_BLOCK_CAUSAL, BLOCKMASK_TILE,
+    SCHED_NO_PAIRING, SCHED_NO_XCD_REMAP, SCHED_REVERSE, SCHED_ALL,
     TILE_EMPTY, TILE_PARTIAL, TILE_FULL,
     attn_fwd, attn_fwd_blockmask, attn_build_blockmask, attn_blockmask_bytes,
     attn_decode_splitkv, attn_decode_combine, attn_decode_num_splits,

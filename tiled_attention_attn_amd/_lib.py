@@ -27,6 +27,10 @@ MASK_CAUSAL = 1
 MASK_WINDOW = 2
 MASK_DOCUMENT = 4
 MASK_BLOCK_CAUSAL = 8
+SCHED_NO_PAIRING = 1 << 16
+SCHED_NO_XCD_REMAP = 1 << 17
+SCHED_REVERSE = 1 << 18
+SCHED_ALL = SCHED_NO_PAIRING | SCHED_NO_XCD_REMAP | SCHED_REVERSE
 BLOCKMASK_TILE = 128
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 
@@ -249,6 +253,7 @@ class Mask:
     window: tuple | None = None
     block_size: int | None = None
     doc_offsets: torch.Tensor | None = None
+    schedule: int = 0  # ATTN_SCHED_* bits: another work-group schedule, results bitwise unchanged
 
     def desc(self) -> attn_mask_desc:
         d = attn_mask_desc()
@@ -258,6 +263,9 @@ class Mask:
         d.doc_offsets = None
         d.num_docs = 0
         d.doc_stride = 0
+        if self.schedule & ~SCHED_ALL:
+            raise ValueError("unknown schedule bits")
+        d.flags |= self.schedule
         if self.causal:
             d.flags |= MASK_CAUSAL
         if self.window is not None:

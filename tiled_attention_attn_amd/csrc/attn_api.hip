@@ -41,12 +41,16 @@ int check_dtype(int dtype) {
   return (dtype == ATTN_DTYPE_BF16 || dtype == ATTN_DTYPE_F16) ? ATTN_OK : ATTN_ERR_DTYPE;
 }
 
-// Converts the public mask descriptor; `allow_doc` is false for decode.
-int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParams& out) {
+// Converts the public mask descriptor; `allow_doc` is false for decode.  The
+// schedule bits go to `sched` (0 when there are none).
+int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParams& out,
+              uint32_t* sched = nullptr) {
   out = MaskParams{0u, -1, -1, 1, nullptr, 1, 2};
+  if (sched) *sched = 0u;
   if (m == nullptr) return ATTN_OK;
-  if (m->flags & ~ATTN_MASK_ALL) return ATTN_ERR_MASK;
-  out.flags = m->flags;
+  if (m->flags & ~(ATTN_MASK_ALL | ATTN_SCHED_ALL)) return ATTN_ERR_MASK;
+  out.flags = m->flags & ATTN_MASK_ALL;
+  if (sched) *sched = m->flags & ATTN_SCHED_ALL;
   out.wl = m->window_left < 0 ? -1 : m->window_left;
   out.wr = m->window_right < 0 ? -1 : m->window_right;
   if (m->flags & ATTN_MASK_BLOCK_CAUSAL) {
@@ -150,10 +154,10 @@ bool causal_like(const MaskParams& m) {
 }
 
 void set_slots(FwdParams& p, bool paired) {
-  p.paired = paired && p.n_qt > 1;
+  p.paired = paired && p.n_qt > 1 && !(p.sched & ATTN_SCHED_NO_PAIRING);
   p.n_slots = p.paired ? (p.n_qt + 1) / 2 : p.n_qt;
   const long units = (long)p.B * p.Hq * p.n_slots;
-  p.xcd_remap = (units % 8) == 0;
+  p.xcd_remap = (units % 8) == 0 && !(p.sched & ATTN_SCHED_NO_XCD_REMAP);
 }
 
 // Shape-based choice of attn_fwd_auto.  A decode-shaped call -- all G * Nq
@@ -226,7 +230,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
                         D, dtype, scale);
   if (st) return st;
   FwdParams p;
-  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
   if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
@@ -280,7 +284,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   if (bm->nQt != (Nq + 127) / 128 || bm->nKt != (Nk + 127) / 128) return ATTN_ERR_BLOCKMASK;
   if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
   FwdParams p;
-  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
   if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
@@ -346,7 +350,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   if ((max_pages + num_splits - 1) / num_splits > 2048) return ATTN_ERR_WORKSPACE;
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
-  if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask))) return st;
+  if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask, &p.sched))) return st;
   if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
@@ -419,7 +423,7 @@ int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
     return attn_fwd(q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk,
                     D, dtype, scale, mask, smod, stream);
   DecParams p;
-  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
   if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (workspace == nullptr) return ATTN_ERR_NULL;
@@ -486,7 +490,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
     return ATTN_ERR_STRIDE;
   if ((st = check_scale(scale))) return st;
   BwdParams p;
-  if ((st = make_mask(mask, Nq, Nk, true, p.mask))) return st;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
   if ((st = make_smod(smod, scale, true, Hq / Hkv, D == 64, p.smod))) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
@@ -515,15 +519,16 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   p.ws_delta = workspace + (size_t)B * Hq * p.nq_pad;
   // Causal-like masks give later query tiles more keys and earlier key tiles
   // more rows: pair tile i with n-1-i in both kernels.
-  const bool pair = causal_like(p.mask);
+  const bool pair = causal_like(p.mask) && !(p.sched & ATTN_SCHED_NO_PAIRING);
+  const bool remap = !(p.sched & ATTN_SCHED_NO_XCD_REMAP);
   p.n_kt = (Nk + 127) / 128;
   p.kv_paired = pair && p.n_kt > 1;
   p.kv_slots = p.kv_paired ? (p.n_kt + 1) / 2 : p.n_kt;
-  p.kv_xcd_remap = ((long)B * Hkv * p.kv_slots) % 8 == 0;
+  p.kv_xcd_remap = remap && ((long)B * Hkv * p.kv_slots) % 8 == 0;
   p.n_qt = (Nq + 127) / 128;
   p.q_paired = pair && p.n_qt > 1;
   p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
-  p.q_xcd_remap = ((long)B * Hq * p.q_slots) % 8 == 0;
+  p.q_xcd_remap = remap && ((long)B * Hq * p.q_slots) % 8 == 0;
   // dQ groups B Hq n_qt, dK/dV groups B Hkv n_kt, Delta threads 8 per padded row
   if (!grid_fits((int64_t)B * Hq * p.n_qt) || !grid_fits((int64_t)B * Hkv * p.n_kt) ||
       !grid_fits(((int64_t)B * Hq * p.nq_pad * 8 + 255) / 256))

@@ -407,11 +407,12 @@ bwd_kv_kernel(const BwdParams p) {
   // the ring (34 KB), then the G bias tables (up to 32 KB) when SM
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES + (SM ? kMaxRelTables * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
-  int unit = blockIdx.x;
+  const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  int unit = id;
   if (p.kv_xcd_remap) {
     // whole KV heads per XCD, so their Q / dO tiles stay in one L2
     const int per = gridDim.x >> 3;
-    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    unit = (id & 7) * per + (id >> 3);
   }
   const int slot = unit % p.kv_slots;
   const int r = unit / p.kv_slots;
@@ -646,10 +647,11 @@ bwd_q_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024)))
   char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
-  int unit = blockIdx.x;
+  const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  int unit = id;
   if (p.q_xcd_remap) {
     const int per = gridDim.x >> 3;
-    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    unit = (id & 7) * per + (id >> 3);
   }
   // unit = ((b * Hkv + kvh) * q_slots + slot) * G + g, as in the forward pass
   const int g = unit % p.G;

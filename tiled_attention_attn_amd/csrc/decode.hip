@@ -75,8 +75,11 @@ decode_kernel(const DecParams p) {
     return smem + (st % NST) * 2 * TILE_BYTES + TILE_BYTES;
   };
 
-  const int s = blockIdx.x % p.S, rg = blockIdx.x / p.S;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const bool rev = (p.sched & ATTN_SCHED_REVERSE) != 0;
+  const int bx = rev ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int s = bx % p.S, rg = bx / p.S;
+  const int kvh = rev ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int b = rev ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 4, col = lane & 15;
 

@@ -387,12 +387,13 @@ fwd_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(1024)))
   char smem_raw[NST * 2 * KBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
-  int unit = blockIdx.x;
+  const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  int unit = id;
   if (p.xcd_remap) {
     // work groups are dealt round-robin to the 8 XCDs: give each XCD a
     // contiguous range of units (whole KV heads) so K/V stay in one L2.
     const int per = gridDim.x >> 3;
-    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    unit = (id & 7) * per + (id >> 3);
   }
   // unit = ((b * Hkv + kvh) * n_slots + slot) * G + g: the G query heads that
   // share a KV head are adjacent, so the work groups of one query tile for

@@ -351,12 +351,13 @@ fwd_pp_kernel(const FwdParams p) {
   __shared__ __attribute__((aligned(1024)))
   char smem_raw[kPPStages * 2 * PPKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
-  int unit = blockIdx.x;
+  const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  int unit = id;
   if (p.xcd_remap) {
     // work groups are dealt round-robin to the 8 XCDs: give each XCD a
     // contiguous range of units (whole KV heads) so K/V stay in one L2.
     const int per = gridDim.x >> 3;
-    unit = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    unit = (id & 7) * per + (id >> 3);
   }
   // unit = ((b * Hkv + kvh) * n_slots + slot) * G + g (query heads of one KV
   // head adjacent).
@@ -386,7 +387,7 @@ int launch_fwd_pp(const FwdParams& p_in, int D, int dtype, hipStream_t stream) {
   p.paired = p_in.paired && p.n_qt > 1;
   p.n_slots = p.paired ? (p.n_qt + 1) / 2 : p.n_qt;
   const long units = (long)p.B * p.Hq * p.n_slots;
-  p.xcd_remap = (units % 8) == 0;
+  p.xcd_remap = (units % 8) == 0 && !(p.sched & ATTN_SCHED_NO_XCD_REMAP);
   dim3 grid((unsigned)units), block(kPPThreads);
   if (D != 128) return ATTN_ERR_HEAD_DIM;  // D=64 prefill runs on fwd_kernel
   const bool sm = p.smod.flags != 0;

@@ -29,6 +29,7 @@ struct FwdParams {
   int n_slots;  // work groups per (batch, head)
   int paired;   // slot i also does tile n_qt-1-i
   int xcd_remap;
+  uint32_t sched;  // ATTN_SCHED_* bits of the call
 };
 
 // BlockMask builder.
@@ -67,6 +68,7 @@ struct DecParams {
   ScoreParams smod;
   float* ws_o;
   float* ws_lse;
+  uint32_t sched;  // ATTN_SCHED_* bits of the call
 };
 
 // Backward pass (dQ, dK, dV by recomputation).
@@ -92,6 +94,7 @@ struct BwdParams {
   float* ws_delta;  // [B*Hq][nq_pad]: rowsum(dO * O); 0 for padding
   int n_kt, kv_slots, kv_paired, kv_xcd_remap;  // 128-key tiles (dK / dV kernel)
   int n_qt, q_slots, q_paired, q_xcd_remap;     // 128-row tiles (dQ kernel)
+  uint32_t sched;  // ATTN_SCHED_* bits of the call
 };
 
 }  // namespace tattn
