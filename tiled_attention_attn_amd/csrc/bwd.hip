@@ -405,7 +405,9 @@ __attribute__((amdgpu_waves_per_eu(BwdKvOcc<D>::value, BwdKvOcc<D>::value)))
 bwd_kv_kernel(const BwdParams p) {
   constexpr int STAGE_BYTES = 2 * BwdQRows<D>::value * D * 2 + 1024;
   // the ring (34 KB), then the G bias tables (up to 32 KB) when SM
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE_BYTES + (SM ? kMaxRelTables * 4 : 0)];
+  constexpr int LDS_BYTES = 2 * STAGE_BYTES + (SM ? kMaxRelTables * 4 : 0);
+  static_assert(2 * STAGE_BYTES <= kLdsCopyLimit && LDS_BYTES <= kLdsFootprintLimit, "LDS limits");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   int unit = id;
@@ -644,8 +646,10 @@ template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(const BwdParams p) {
   // the ring (64 KB), then the head's bias table (8 KB) when SM
-  __shared__ __attribute__((aligned(1024)))
-  char smem_raw[2 * 2 * BwdKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
+  constexpr int RING = 2 * 2 * BwdKBlk<D>::value * D * 2;
+  constexpr int LDS_BYTES = RING + (SM ? kMaxRelTable * 4 : 0);
+  static_assert(RING <= kLdsCopyLimit && LDS_BYTES <= kLdsFootprintLimit, "LDS limits");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   int unit = id;

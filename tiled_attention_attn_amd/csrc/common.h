@@ -141,6 +141,17 @@ __device__ __forceinline__ void wait_vmem_le() {
   asm volatile("" ::: "memory");
 }
 
+// ---- LDS limits ----------------------------------------------------------------
+// Every kernel keeps two limits, checked at compile time beside its LDS
+// declaration: its asynchronous global -> LDS copies land only in the first
+// 64 KB of the work group's LDS (the copy ring is the work group's first,
+// 1024-byte aligned LDS object), and its whole LDS footprint stays at or under
+// 72 KB.  A build that broke both (a 136 KB decode footprint with copies at
+// 64-128 KB) faulted the GPU; which of the two properties mattered was not
+// isolated, so both are kept.
+constexpr int kLdsCopyLimit = 64 * 1024;
+constexpr int kLdsFootprintLimit = 72 * 1024;
+
 // ---- cross-lane ----------------------------------------------------------------
 // Value of the lane 32 positions away (lanes l and l^32 exchange).
 __device__ __forceinline__ float other_half(float x) {

@@ -67,6 +67,9 @@ decode_kernel(const DecParams p) {
   constexpr int NC = D / 32;   // d-chunks of the QK MFMA (K = 32)
   constexpr int NDB = D / 16;  // d-blocks of the PV MFMA (M = 16)
   constexpr int NST = kDecStages;
+  static_assert(NST * 2 * TILE_BYTES <= kLdsCopyLimit &&
+                    NST * 2 * TILE_BYTES + kDecMaxSplitPages * 4 <= kLdsFootprintLimit,
+                "LDS limits");
   __shared__ __attribute__((aligned(1024))) char smem_raw[NST * 2 * TILE_BYTES];
   __shared__ int s_pages[kDecMaxSplitPages];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;

@@ -348,8 +348,10 @@ template <int D, typename T, bool SM>
 __global__ void __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_pp_kernel(const FwdParams p) {
   // the ring (64 KB), then the score-change table (8 KB) when SM
-  __shared__ __attribute__((aligned(1024)))
-  char smem_raw[kPPStages * 2 * PPKBlk<D>::value * D * 2 + (SM ? kMaxRelTable * 4 : 0)];
+  constexpr int RING = kPPStages * 2 * PPKBlk<D>::value * D * 2;
+  constexpr int LDS_BYTES = RING + (SM ? kMaxRelTable * 4 : 0);
+  static_assert(RING <= kLdsCopyLimit && LDS_BYTES <= kLdsFootprintLimit, "LDS limits");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[LDS_BYTES];
   TATTN_LDS char* smem = (TATTN_LDS char*)smem_raw;
   const int id = (p.sched & ATTN_SCHED_REVERSE) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
   int unit = id;
