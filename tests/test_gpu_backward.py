@@ -120,6 +120,9 @@ CASES = [
     ("block_diffusion_d128", 1, 2, 2, 400, 400, 128, {"block": 16}),
     ("block_diffusion_d64_bs5", 1, 1, 1, 333, 333, 64, {"block": 5}),
     ("causal_window_d64", 1, 2, 2, 640, 640, 64, {"causal": True, "window": (200, 0)}),
+    # A window mask without documents whose dK/dV row searches once branched into the
+    # document search and read through the null offsets pointer (work group 1).
+    ("window_b2_gqa2_d64_n520", 2, 2, 1, 520, 520, 64, {"window": (100, 100)}),
 ]
 
 

@@ -19,10 +19,12 @@ pytestmark = pytest.mark.gpu
 
 # The prefill and backward kernels at D = 64 are not offered with a score
 # change: a run of these tests faulted the GPU in the D = 64 backward case
-# (symmetric ALiBi + bias table under a window mask) and no cause has been
-# shown yet, so the library rejects D = 64 score changes (ATTN_ERR_SCORE_MOD)
-# and their GPU cases are skipped until one is.
-D64_OFF = "score changes at D=64 are switched off after an unexplained GPU fault"
+# (symmetric ALiBi + bias table under a window mask).  The cause, found by
+# replaying the compiled dK/dV kernel on the CPU, was its row search branching
+# on a lane mask made under another EXEC; that search is fixed, but the library
+# keeps rejecting D = 64 score changes (ATTN_ERR_SCORE_MOD) until a GPU run of
+# these cases confirms the fix.
+D64_OFF = "score changes at D=64 stay switched off until a GPU run confirms the row-search fix"
 
 if torch.cuda.is_available():  # with a GPU present the HIP library must load: no fallback
     import tiled_attention_attn_amd as T

@@ -72,8 +72,10 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
 // Converts the public score_mod descriptor.  `allow_rel` is false for
 // decode; `G_bwd` > 0 (the backward pass) also bounds the G tables one
 // work group stages.  `prefill_d64`: the prefill and backward kernels at
-// D = 64 are not offered with a score change (their score-change variants
-// are switched off after a GPU memory fault whose cause is not yet found).
+// D = 64 are not offered with a score change.  Their variants were switched
+// off after a GPU memory fault, traced since to the dK/dV kernel's row search
+// (a branch on a lane mask made under another EXEC, now removed); they stay
+// off until a GPU run confirms that fix.
 int make_smod(const attn_score_mod* m, float scale, bool allow_rel, int G_bwd, bool prefill_d64,
               ScoreParams& out) {
   out = ScoreParams{0u, nullptr, nullptr, 0, 0.f, 0.f};

@@ -80,27 +80,84 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_pre_kernel(const BwdParams p)
   }
 }
 
+// The searches below run in every lane with the lane's own key.  Written as
+// while-loops they leave the loop lane by lane, and the compiled dK / dV
+// kernel then evaluated a mask-flag test of the inlined row_interval as a lane
+// mask under one loop's shrinking EXEC and branched on that mask in the next
+// loop, where it could hold no active lane: the document search then ran for
+// a mask without documents and read through its null offsets pointer.  So
+// every loop here runs a wave-uniform number of steps and moves its bounds
+// with selects; no branch depends on a lane mask made under another EXEC.
+
+// Steps that shrink a search over n + 1 candidates to one: the bit length of n.
+__device__ __forceinline__ int search_steps(int n) {
+  return n > 0 ? 32 - __builtin_clz((unsigned)n) : 0;
+}
+
+// row_interval with its document search run for doc_steps = search_steps(num_docs - 1)
+// steps (each step keeps at least half of the range minus one candidate).
+__device__ __forceinline__ void row_interval_fixed(const MaskParams& m, int b, int64_t p, int Nk,
+                                                   int doc_steps, int& lo_out, int& hi_out) {
+  int64_t lo = 0, hi = (int64_t)Nk - 1;
+  if (m.flags & ATTN_MASK_CAUSAL) hi = hi < p ? hi : p;
+  if (m.flags & ATTN_MASK_WINDOW) {
+    if (m.wl >= 0) { int64_t a = p - m.wl; lo = lo > a ? lo : a; }
+    if (m.wr >= 0) { int64_t a = p + m.wr; hi = hi < a ? hi : a; }
+  }
+  if (m.flags & ATTN_MASK_BLOCK_CAUSAL) {
+    int64_t a = (floordiv(p, m.bs) + 1) * m.bs - 1;
+    hi = hi < a ? hi : a;
+  }
+  if ((m.flags & ATTN_MASK_DOCUMENT) && Nk > 0) {
+    const int32_t* off = m.doc + (int64_t)b * m.doc_stride;
+    int64_t pc = p < 0 ? 0 : (p >= Nk ? Nk - 1 : p);
+    // largest d in [0, num_docs) with off[d] <= pc; mid stays inside [lo_d, hi_d]
+    int lo_d = 0, hi_d = m.num_docs - 1;
+    for (int it = 0; it < doc_steps; ++it) {
+      const int mid = (lo_d + hi_d + 1) >> 1;
+      const bool go = lo_d < hi_d;
+      const bool le = off[mid] <= pc;
+      lo_d = go && le ? mid : lo_d;
+      hi_d = go && !le ? mid - 1 : hi_d;
+    }
+    int64_t s = off[lo_d], e = (int64_t)off[lo_d + 1] - 1;
+    lo = lo > s ? lo : s;
+    hi = hi < e ? hi : e;
+  }
+  if (lo < 0) lo = 0;
+  if (hi > (int64_t)Nk - 1) hi = (int64_t)Nk - 1;
+  lo_out = (int)lo;
+  hi_out = (int)hi;
+}
+
 // Rows that see key `key`: [qa, qb] (empty when qa > qb).  hi(row) never
 // decreases, so {row : hi >= key} is a suffix of the rows; lo(row) never
 // decreases, so {row : lo <= key} is a prefix; the rows seeing the key are
-// their intersection.
+// their intersection.  Each search takes search_steps(Nq) steps: a step
+// leaves at most half of the z - a remaining candidates beyond the first.
 __device__ __forceinline__ void key_rows(const MaskParams& m, int b, int key, int Nq, int Nk,
                                          int64_t shift, int& qa, int& qb) {
+  const int steps = search_steps(Nq);
+  const int doc_steps = (m.flags & ATTN_MASK_DOCUMENT) ? search_steps(m.num_docs - 1) : 0;
   int a = 0, z = Nq;  // first row with hi >= key (Nq if none)
-  while (a < z) {
+  for (int it = 0; it < steps; ++it) {
     const int mid = (a + z) >> 1;
     int l, h;
-    row_interval(m, b, mid + shift, Nk, l, h);
-    if (h >= key) z = mid; else a = mid + 1;
+    row_interval_fixed(m, b, mid + shift, Nk, doc_steps, l, h);
+    const bool go = a < z, right = h >= key;
+    z = go && right ? mid : z;
+    a = go && !right ? mid + 1 : a;
   }
   qa = a;
   a = -1;
   z = Nq - 1;  // last row with lo <= key (-1 if none)
-  while (a < z) {
+  for (int it = 0; it < steps; ++it) {
     const int mid = (a + z + 1) >> 1;
     int l, h;
-    row_interval(m, b, mid + shift, Nk, l, h);
-    if (l <= key) a = mid; else z = mid - 1;
+    row_interval_fixed(m, b, mid + shift, Nk, doc_steps, l, h);
+    const bool go = a < z, left = l <= key;
+    a = go && left ? mid : a;
+    z = go && !left ? mid - 1 : z;
   }
   qb = a;
 }
@@ -157,9 +214,11 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
         stage_rel_table(p.smod, kvh * p.G + g, tabs + g * (2 * p.smod.R + 1), tid, kBwdThreads);
   }
 
-  int qa = 0x3fffffff, qb = -1;
-  if (key_ok) key_rows(p.mask, b, key, p.Nq, p.Nk, shift, qa, qb);
-  if (qa > qb) { qa = 0x3fffffff; qb = -1; }
+  // Every lane searches (a key past Nk searches for key Nk - 1), so the
+  // search runs outside any lane-dependent branch.
+  int qa, qb;
+  key_rows(p.mask, b, key_ok ? key : p.Nk - 1, p.Nq, p.Nk, shift, qa, qb);
+  if (!key_ok || qa > qb) { qa = 0x3fffffff; qb = -1; }
   // Wave bounds, wave-uniform (scalar registers): rows any lane sees
   // [w_lo, w_hi]; rows every lane sees [w_lo_max, w_hi_min].
   int w_lo = qa, w_hi = qb, w_lo_max = qa, w_hi_min = qb;
