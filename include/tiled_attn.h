@@ -145,8 +145,7 @@ typedef struct attn_mask_desc {
  * and treats the biases and the cap as constants (no gradient for them).
  * SOFTCAP needs a finite softcap > 0.
  * REL_BIAS needs 0 <= R <= 1023 and, in attn_bwd, (Hq / Hkv) * (2R + 1) <=
- * 8192.  attn_fwd, attn_fwd_blockmask and attn_bwd take a score change at
- * D = 128 only (ATTN_ERR_SCORE_MOD at D = 64); attn_decode_splitkv takes
+ * 8192.  attn_fwd, attn_fwd_blockmask, attn_bwd and attn_decode_splitkv take
  * every score change at D = 64 and 128.
  */
 #define ATTN_SCORE_ALIBI 1u

@@ -73,13 +73,13 @@ def test_fwd_argument_errors(T):
     assert f128(smod=SMD(flags=16)) == -13                                   # unknown flag
     for cap in (0.0, -3.0, float("inf"), float("nan")):                      # SOFTCAP needs a cap > 0
         assert f128(smod=SMD(flags=8, softcap=cap)) == -13
-    assert _fwd(T, smod=SMD(flags=8, softcap=30.0)) == -13                   # not at D = 64
+    assert _fwd(T, smod=SMD(flags=8, softcap=30.0), B=0) == 0               # D = 64 takes a cap
     assert f128(smod=SMD(flags=3, slopes=16)) == -13                         # ALIBI and ALIBI_SYM
     assert f128(smod=SMD(flags=1, slopes=None)) == -1
     assert f128(smod=SMD(flags=4, rel_bias=None, rel_radius=3)) == -1
     assert f128(smod=SMD(flags=4, rel_bias=16, rel_radius=1024)) == -13     # 2R+1 > 2048
     assert f128(smod=SMD(flags=4, rel_bias=16, rel_radius=-1)) == -13
-    assert _fwd(T, smod=SMD(flags=1, slopes=16)) == -13                      # D = 64 takes no score change
+    assert _fwd(T, smod=SMD(flags=1, slopes=16), B=0) == 0                  # and ALiBi (validated, B = 0)
     assert f128(smod=SMD(flags=0), B=0) == 0
     assert _fwd(T, Hq=3, Hkv=2) == -4
     assert _fwd(T, Hkv=0) == -4
@@ -202,7 +202,7 @@ def test_bwd_argument_errors(T):
     q128 = _strides(128 * 256, 128 * 256, 128)
     assert bwd(D=128, s=q128, ks=q128, Hq=8, Hkv=1,
                smod=T.attn_score_mod(flags=4, rel_bias=16, rel_radius=512)) == -13
-    assert bwd(smod=T.attn_score_mod(flags=1, slopes=16)) == -13      # D = 64 takes no score change
+    assert bwd(smod=T.attn_score_mod(flags=1, slopes=16), B=0) == 0   # D = 64 takes a score change
     assert bwd(Hq=2, Hkv=3) == -4
     assert bwd(s=_strides(64 * 256, 64 * 256, 68)) == -5
     assert bwd(ks=_strides(1 << 30, 1 << 30, 1 << 24)) == -5  # streamed row stride over 2^24
@@ -292,8 +292,9 @@ def test_auto_argument_errors(T):
     assert auto(scale=float("nan")) == -11
     assert auto(mask=T.attn_mask_desc(flags=64)) == -7
     assert auto(smod=T.attn_score_mod(flags=1, slopes=None)) == -1
-    # the prefill path keeps attn_fwd's rules: no score change at D = 64
-    assert auto(Nq=4096, D=64, smod=T.attn_score_mod(flags=1, slopes=16)) == -13
+    # the prefill path keeps attn_fwd's rules: a score change at D = 64 is validated like any other
+    assert auto(Nq=4096, D=64, smod=T.attn_score_mod(flags=16)) == -13
+    assert auto(Nq=4096, D=64, B=0, smod=T.attn_score_mod(flags=1, slopes=16)) == 0
     assert auto(B=0) == 0 and auto(Nq=0, ws=None) == 0
 
 

@@ -17,15 +17,6 @@ from test_gpu_backward import _fwd_bwd, assert_grad_close, fp16_floor
 
 pytestmark = pytest.mark.gpu
 
-# The prefill and backward kernels at D = 64 are not offered with a score
-# change: a run of these tests faulted the GPU in the D = 64 backward case
-# (symmetric ALiBi + bias table under a window mask).  The cause, found by
-# replaying the compiled dK/dV kernel on the CPU, was its row search branching
-# on a lane mask made under another EXEC; that search is fixed, but the library
-# keeps rejecting D = 64 score changes (ATTN_ERR_SCORE_MOD) until a GPU run of
-# these cases confirms the fix.
-D64_OFF = "score changes at D=64 stay switched off until a GPU run confirms the row-search fix"
-
 if torch.cuda.is_available():  # with a GPU present the HIP library must load: no fallback
     import tiled_attention_attn_amd as T
 DEV = "cuda"
@@ -82,8 +73,6 @@ PREFILL = [
 @pytest.mark.parametrize("case", PREFILL, ids=[c[0] for c in PREFILL])
 def test_prefill_score_mod(case, dtype):
     name, B, Hq, Hkv, Nq, Nk, D, mspec, kind = case
-    if D == 64:
-        pytest.skip(D64_OFF)
     if dtype == torch.float16 and name not in ("alibi_causal_d128", "rel_alibi_sym_docs_d128",
                                                "cap_alibi_sym_window_d128_gqa"):
         pytest.skip("fp16 checked on a subset")
@@ -102,15 +91,6 @@ def test_prefill_score_mod(case, dtype):
     torch.cuda.synchronize()
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod, score_mod=smod)
     assert_close(f64(o), f64(lse), ro, rl, name)
-
-
-def test_d64_score_change_rejected():
-    """D = 64 prefill / backward calls with a score change fail on the host, before any launch."""
-    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device=DEV)
-    sg = T.ScoreMod(alibi_slopes=alibi_slopes(2).to(DEV))
-    with pytest.raises(T.AttnError) as e:
-        T.attn_fwd(q, q, q, torch.empty_like(q), None, 0.125, None, smod=sg)
-    assert e.value.status == -13
 
 
 @pytest.mark.parametrize("kind", ["alibi+rel", "cap+alibi+rel"])
@@ -256,8 +236,6 @@ BACKWARD = [
 @pytest.mark.parametrize("case", BACKWARD, ids=[c[0] for c in BACKWARD])
 def test_backward_score_mod(case):
     name, B, Hq, Hkv, Nq, Nk, D, mspec, kind, dt = case
-    if D == 64:
-        pytest.skip(D64_OFF)
     announce(f"score_mod backward {name}")
     dtype = torch.float16 if dt == "fp16" else torch.bfloat16
     g = W.generator(zlib.crc32(name.encode()) % 9973)

@@ -69,24 +69,16 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
   return ATTN_OK;
 }
 
-// Converts the public score_mod descriptor.  `allow_rel` is false for
-// decode; `G_bwd` > 0 (the backward pass) also bounds the G tables one
-// work group stages.  `prefill_d64`: the prefill and backward kernels at
-// D = 64 are not offered with a score change.  Their variants were switched
-// off after a GPU memory fault, traced since to the dK/dV kernel's row search
-// (a branch on a lane mask made under another EXEC, now removed); they stay
-// off until a GPU run confirms that fix.
-int make_smod(const attn_score_mod* m, float scale, bool allow_rel, int G_bwd, bool prefill_d64,
-              ScoreParams& out) {
+// Converts the public score_mod descriptor.  `G_bwd` > 0 (the backward
+// pass) also bounds the G bias tables one work group stages.
+int make_smod(const attn_score_mod* m, float scale, int G_bwd, ScoreParams& out) {
   out = ScoreParams{0u, nullptr, nullptr, 0, 0.f, 0.f};
   if (m == nullptr || m->flags == 0) return ATTN_OK;
   const uint32_t f = m->flags;
-  if (prefill_d64) return ATTN_ERR_SCORE_MOD;
   if (f & ~ATTN_SCORE_ALL) return ATTN_ERR_SCORE_MOD;
   if ((f & ATTN_SCORE_ALIBI) && (f & ATTN_SCORE_ALIBI_SYM)) return ATTN_ERR_SCORE_MOD;
   if ((f & (ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM)) && m->slopes == nullptr) return ATTN_ERR_NULL;
   if (f & ATTN_SCORE_REL_BIAS) {
-    if (!allow_rel) return ATTN_ERR_SCORE_MOD;
     if (m->rel_bias == nullptr) return ATTN_ERR_NULL;
     if (m->rel_radius < 0 || 2 * m->rel_radius + 1 > kMaxRelTable) return ATTN_ERR_SCORE_MOD;
     if (G_bwd > 0 && (int64_t)G_bwd * (2 * m->rel_radius + 1) > 8192) return ATTN_ERR_SCORE_MOD;
@@ -233,7 +225,7 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if (st) return st;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, 0, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
@@ -287,7 +279,7 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
   if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
   FwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, true, 0, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, 0, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (!grid_fits((int64_t)B * Hq * ((Nq + 127) / 128))) return ATTN_ERR_SHAPE;
   fill_fwd(p, q, q_stride, k, k_stride, v, v_stride, o, o_stride, lse, B, Hq, Hkv, Nq, Nk, scale);
@@ -353,7 +345,7 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   DecParams p;
   attn_mask_desc causal = {ATTN_MASK_CAUSAL, -1, -1, 0, nullptr, 0, 0};
   if ((st = make_mask(mask ? mask : &causal, 0, 0, false, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, 0, p.smod))) return st;
   if (B == 0 || Lq == 0) return ATTN_OK;
   const int G = Hq / Hkv;
   p.q = q;
@@ -426,7 +418,7 @@ int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
                     D, dtype, scale, mask, smod, stream);
   DecParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, true, 0, false, p.smod))) return st;
+  if ((st = make_smod(smod, scale, 0, p.smod))) return st;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (workspace == nullptr) return ATTN_ERR_NULL;
   if (workspace_bytes < pl.ws_bytes) return ATTN_ERR_WORKSPACE;
@@ -493,7 +485,7 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
   if ((st = check_scale(scale))) return st;
   BwdParams p;
   if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, true, Hq / Hkv, D == 64, p.smod))) return st;
+  if ((st = make_smod(smod, scale, Hq / Hkv, p.smod))) return st;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
   if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
   p.q = q;
