@@ -1,0 +1,153 @@
+"""CPU replays of the compiled backward kernels (tests/isa_replay), and pins of the
+replay's own checks.
+
+The dK/dV kernel's row searches once compiled to code that evaluated the "mask has
+documents" test as a lane mask inside a loop whose lanes leave one by one, and branched
+on it in the next loop under another EXEC.  For the window-masked call below the two
+lane sets were disjoint: the kernel took the document search and read through the null
+offsets pointer.  These tests replay the library's compiled kernels, with the launch
+arguments its host code computes, and require no out-of-bounds access, no lane-mask
+reuse and gradients within the GPU tests' bar of the fp64 oracle.
+"""
+import ctypes
+import math
+import os
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward as OBW, masks as M
+import workloads as W
+
+HAVE_HIPCC = shutil.which("hipcc") is not None or os.path.exists("/opt/rocm/bin/hipcc")
+REL = 2.0 ** -7  # the gradient bar of the GPU backward tests: 2^-7 times the oracle's sum of |terms|
+
+
+def _strides(t):
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
+def _check_grad(got, ref, mag, what):
+    err = np.abs(got.to(torch.float64).numpy() - ref)
+    bad = err > REL * mag
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {err.size} elements over the bar"
+
+
+def _backward_replay(B, Hq, Hkv, N, D, mask_flags, window=None, docs=None, kernels=None, seed=0):
+    """attn_bwd through the recorded host library, then a replay of its launches."""
+    from isa_replay.host import Replay
+    from tiled_attention_attn_amd import _lib
+    rp = Replay(("bwd",))
+    g = W.generator(seed)
+    q, k, v, do = (W.randn_bf16(g, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D), (B, Hq, N, D)))
+    scale = 1.0 / math.sqrt(D)
+    mods, desc = [], _lib.attn_mask_desc(flags=mask_flags, window_left=-1, window_right=-1)
+    if window is not None:
+        desc.window_left, desc.window_right = window
+        mods.append(M.window(window[0], window[1], N, N))
+    off = None
+    if docs is not None:
+        nd = max(len(d) for d in docs)
+        rows = [np.concatenate([[0], np.cumsum(d), np.full(nd - len(d), sum(d))]) for d in docs]
+        off = torch.tensor(np.stack(rows), dtype=torch.int32)
+        desc.doc_offsets, desc.num_docs, desc.doc_stride = off.data_ptr(), nd, off.stride(0)
+        mods.append(M.document(docs, N, N))
+    mod = M.and_(*mods)
+    ro, rl = oracle.attention(*(x.to(torch.float64).numpy() for x in (q, k, v)), scale, mod)
+    o = torch.from_numpy(ro).to(torch.bfloat16)
+    lse = torch.from_numpy(rl).to(torch.float32)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    ws = torch.zeros(max(int(rp.lib.attn_bwd_workspace_bytes(B, Hq, N)) // 4, 1))
+    rp.register(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws, doc_offsets=off)
+    st = rp.lib.attn_bwd(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                         o.data_ptr(), _strides(o), do.data_ptr(), _strides(do), lse.data_ptr(),
+                         dq.data_ptr(), _strides(dq), dk.data_ptr(), _strides(dk), dv.data_ptr(), _strides(dv),
+                         B, Hq, Hkv, N, N, D, 0, scale, ctypes.byref(desc), None, ws.data_ptr(), ws.numel() * 4,
+                         None)
+    assert st == 0, st
+    rp.run(only=kernels)
+    ref = OBW.attention_bwd(*(x.to(torch.float64).numpy() for x in (q, k, v, do)), scale, mod,
+                            row_block=256, bound=True, o_used=o.to(torch.float64).numpy())
+    return rp, (dq, dk, dv), ref
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_window_mask_backward_d64_replays_clean():
+    """The shape whose dK/dV row search read through the null document pointer: every
+    kernel of the call replays without a fault or a lane-mask note, within the bar."""
+    rp, (dq, dk, dv), (rq, rk, rv, (mq, mk, mv)) = _backward_replay(
+        2, 2, 1, 520, 64, 2, window=(100, 100), seed=11)
+    assert [r[0].split("kernel")[0] for r in rp.ran] == ["_ZN5tattn14bwd_pre_", "_ZN5tattn13bwd_kv_",
+                                                          "_ZN5tattn12bwd_q_"]
+    assert not rp.notes, rp.notes
+    _check_grad(dq, rq, mq, "dQ")
+    _check_grad(dk, rk, mk, "dK")
+    _check_grad(dv, rv, mv, "dV")
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_window_and_documents_backward_d128_replays_clean():
+    """D = 128 with documents (the search's document steps run): the dK/dV kernel replays
+    without a fault or a lane-mask note, within the bar."""
+    rp, (dq, dk, dv), (rq, rk, rv, (mq, mk, mv)) = _backward_replay(
+        2, 2, 2, 520, 128, 2 | 4, window=(64, 64), docs=[[130, 250, 140], [520]], kernels=["bwd_pre", "bwd_kv"],
+        seed=12)
+    assert not rp.notes, rp.notes
+    _check_grad(dk, rk, mk, "dK")
+    _check_grad(dv, rv, mv, "dV")
+
+
+# ---- pins of the replay's own checks, on hand-written assembly ----------------------
+_ASM = """\
+probe:
+\ts_load_dwordx2 s[4:5], s[0:1], 0x0
+\tv_cmp_gt_u32_e64 s[6:7], 8, v0
+\ts_and_saveexec_b64 s[8:9], s[6:7]
+\tv_cmp_ne_u32_e64 s[10:11], 1, v0
+\ts_or_b64 exec, exec, s[8:9]
+\ts_and_b64 vcc, exec, s[10:11]
+\ts_waitcnt lgkmcnt(0)
+\tv_mov_b32_e32 v1, s4
+\tv_mov_b32_e32 v2, s5
+\tv_lshlrev_b32_e32 v3, 2, v0
+\tv_add_co_u32_e32 v1, vcc, v1, v3
+\tv_addc_co_u32_e32 v2, vcc, 0, v2, vcc
+\tglobal_load_dword v4, v[1:2], off
+\t{use}
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+def _probe(use, n_words):
+    from isa_replay import emulator as E
+    mem = E.Memory()
+    data = np.arange(n_words, dtype=np.uint32)
+    buf_addr = mem.alloc(data.tobytes(), "buffer")
+    ka = mem.alloc(np.array([buf_addr], dtype=np.uint64).tobytes(), "kernarg")
+    with tempfile.NamedTemporaryFile("w", suffix=".s", delete=False) as fh:
+        fh.write(_ASM.format(use=use))
+    try:
+        m = E.Machine(fh.name, "probe", mem, ka, 0, 64)
+        m.run_group((0, 0, 0), [0])
+    finally:
+        os.unlink(fh.name)
+    return m
+
+
+def test_replay_flags_a_lane_mask_used_under_a_wider_exec():
+    """A mask made under EXEC = lanes 0..7 and tested under all 64 lanes is reported."""
+    m = _probe("s_waitcnt vmcnt(0)", 64)
+    assert len(m.notes) == 1 and "lane mask" in m.notes[0] and "00000000000000ff" in m.notes[0]
+
+
+def test_replay_flags_out_of_bounds_and_unwaited_loads():
+    from isa_replay import emulator as E
+    with pytest.raises(E.Fault, match="outside every allocation"):
+        _probe("s_waitcnt vmcnt(0)", 63)          # lane 63 reads one word past the buffer
+    with pytest.raises(E.Hazard, match="outstanding"):
+        _probe("v_mov_b32_e32 v5, v4", 64)        # uses the load's register before its wait

@@ -87,11 +87,8 @@ class attn_blockmask(ctypes.Structure):
     ]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(
-            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
-    lib = ctypes.CDLL(LIB_PATH)
+def declare_signatures(lib):
+    """Sets the C ABI's argument and result types on a loaded copy of the library."""
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     I64 = ctypes.c_int64
     STR = ctypes.POINTER(ctypes.c_int64)
@@ -125,6 +122,13 @@ def _load():
         fn.restype = res
         fn.argtypes = args
     return lib
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    return declare_signatures(ctypes.CDLL(LIB_PATH))
 
 
 _lib = _load()
