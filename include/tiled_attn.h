@@ -404,6 +404,42 @@ int attn_bwd(const void* q, const int64_t q_stride[3],
 int attn_probe_stream_read(const void* src, size_t bytes, int blocks, uint32_t* sink,
                            hipStream_t stream);
 
+/* ---- backward pass over a BlockMask ------------------------------------------
+ * attn_bwd_blockmask: the gradients of attn_fwd_blockmask's O (same Q, K, V,
+ * mask, score_mod, BlockMask), by the same recomputation as attn_bwd.  The dQ
+ * kernel walks a query tile's FULL / PARTIAL key tiles from `bm` (the forward
+ * lists); the dK / dV kernel walks a key tile's FULL / PARTIAL query tiles from
+ * `bm_t`, the key-tile-major lists attn_blockmask_transpose builds from `bm`.
+ * FULL tiles apply no predicate, PARTIAL tiles the `mask` intervals (the
+ * FlexAttention article, section 1: BlockMask block sparsity; the DeepSeek
+ * v2->v4 article, section 2: segmented recomputation).  Arguments and
+ * workspace as attn_bwd; bm as attn_fwd_blockmask's; bm_t->Bm / Hm equal
+ * bm's and bm_t->nQt = bm->nKt, bm_t->nKt = bm->nQt (ATTN_ERR_BLOCKMASK
+ * otherwise).  No score change is taken here (ATTN_ERR_SCORE_MOD).
+ */
+int attn_bwd_blockmask(const void* q, const int64_t q_stride[3],
+                       const void* k, const int64_t k_stride[3],
+                       const void* v, const int64_t v_stride[3],
+                       const void* o, const int64_t o_stride[3],
+                       const void* d_o, const int64_t do_stride[3], const float* lse,
+                       void* dq, const int64_t dq_stride[3],
+                       void* dk, const int64_t dk_stride[3],
+                       void* dv, const int64_t dv_stride[3],
+                       int B, int Hq, int Hkv, int Nq, int Nk, int D, int dtype, float scale,
+                       const attn_mask_desc* mask, const attn_score_mod* smod,
+                       const attn_blockmask* bm, const attn_blockmask* bm_t,
+                       float* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* attn_blockmask_transpose: fills `out` with the key-tile-major lists of `bm`:
+ * row kt of (batch row, head) lists, ascending, the query tiles whose tile
+ * (qt, kt) is PARTIAL / FULL in `bm`.  out->Bm / Hm must equal bm's, out->nQt
+ * = bm->nKt and out->nKt = bm->nQt; its arrays are caller-allocated
+ * (attn_blockmask_bytes(Bm, Hm, bm->nKt, bm->nQt)).  map_tmp is device memory
+ * of at least Bm * Hm * nQt * nKt bytes, overwritten (a class map).
+ */
+int attn_blockmask_transpose(const attn_blockmask* bm, attn_blockmask* out, uint8_t* map_tmp,
+                             size_t map_tmp_bytes, hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* attn_status_str(int status);
 

@@ -859,6 +859,11 @@ class Semantics:
         a, b, c = (_i32(self.V(w, x)) for x in i.args[1:4])
         self.WV(w, i.args[0], np.minimum(np.minimum(a, b), c).view(U32))
 
+    def op_v_med3_i32(self, w, i):
+        a, b, c = (_i32(self.V(w, x)).astype(np.int64) for x in i.args[1:4])
+        r = np.maximum(np.minimum(a, b), np.minimum(np.maximum(a, b), c))
+        self.WV(w, i.args[0], (r & M32).astype(U32))
+
     def op_v_mul_hi_u32(self, w, i):
         a, b = self.V(w, i.args[1]), self.V(w, i.args[2])
         self.WV(w, i.args[0], np.array([(int(x) * int(y)) >> 32 for x, y in zip(a, b)], dtype=U32))

@@ -217,6 +217,47 @@ def test_bwd_argument_errors(T):
                dk=None, dv=None) == 0
 
 
+def test_bwd_blockmask_and_transpose_argument_errors(T):
+    lib = T.lib_handle()
+    qs = _strides(64 * 256, 64 * 256, 64)
+    ws = T.attn_bwd_workspace_bytes(1, 1, 256)
+    BM = T.attn_blockmask
+
+    def lists(Bm=1, Hm=1, nQt=2, nKt=2, base=512, **kw):
+        a = dict(part_num=base, part_idx=base + 16, full_num=base + 32, full_idx=base + 48)
+        a.update(kw)
+        return BM(Bm=Bm, Hm=Hm, nQt=nQt, nKt=nKt, **a)
+
+    def bwd(bm="d", bm_t="d", **kw):
+        a = dict(B=1, Hq=1, Hkv=1, Nq=256, Nk=256, D=64, smod=None, wsb=ws)
+        a.update(kw)
+        bm = lists() if bm == "d" else bm
+        bm_t = lists(base=1024) if bm_t == "d" else bm_t
+        sm = None if a["smod"] is None else ctypes.byref(a["smod"])
+        ref = lambda x: None if x is None else ctypes.byref(x)
+        return lib.attn_bwd_blockmask(16, qs, 32, qs, 48, qs, 64, qs, 80, qs, 96, 112, qs, 128, qs, 144, qs,
+                                      a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["D"], 0, 0.125, None, sm,
+                                      ref(bm), ref(bm_t), 160, a["wsb"], None)
+    assert bwd(bm=None) == -1 and bwd(bm_t=None) == -1
+    assert bwd(bm_t=lists(base=1024, full_idx=None)) == -1
+    assert bwd(bm=lists(nQt=3)) == -10                     # tile counts must match Nq / Nk
+    assert bwd(bm=lists(Bm=2)) == -10                      # Bm is 1 or B
+    assert bwd(bm_t=lists(base=1024, Hm=2)) == -10         # the transpose must match bm
+    assert bwd(bm=lists(nKt=3), bm_t=lists(base=1024, nKt=3), Nk=300) == -10  # bm_t is bm's nKt x nQt
+    assert bwd(smod=T.attn_score_mod(flags=1, slopes=16)) == -13  # no score change on this path
+    assert bwd(D=96) == -3
+    assert bwd(wsb=ws - 4) == -8
+    assert bwd(B=0) == 0
+    tp = lambda bm, out, tmp=2048, n=1 << 20: lib.attn_blockmask_transpose(
+        None if bm is None else ctypes.byref(bm), None if out is None else ctypes.byref(out), tmp, n, None)
+    assert tp(None, lists()) == -1 and tp(lists(), None) == -1
+    assert tp(lists(nQt=3, nKt=2), lists(base=1024, nQt=3, nKt=2)) == -10   # out must be nKt x nQt
+    assert tp(lists(Hm=2), lists(base=1024)) == -10
+    assert tp(lists(), lists(base=1024), tmp=None) == -1
+    assert tp(lists(), lists(base=1024), n=3) == -8                           # map_tmp holds 4 bytes
+    assert tp(lists(nQt=0, nKt=0), lists(base=1024, nQt=0, nKt=0), tmp=None) == 0
+
+
 def test_grids_beyond_the_launch_limit_are_rejected(T):
     """Shapes whose work-group count passes 2^31 - 1 fail on the host (ATTN_ERR_SHAPE)
     instead of launching a truncated grid."""

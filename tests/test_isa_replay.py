@@ -101,6 +101,64 @@ def test_window_and_documents_backward_d128_replays_clean():
     _check_grad(dv, rv, mv, "dV")
 
 
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_blockmask_backward_per_head_maps_d128_replays_clean():
+    """The BlockMask backward call that faulted on a GPU before the row-search fix: B=2,
+    one tile map per (batch, head), a window predicate on PARTIAL tiles.  The list builder,
+    the transposition and the dK/dV kernel replay without a fault or a lane-mask note;
+    the transposed lists equal the oracle's and dK, dV are within the bar."""
+    from isa_replay.host import Replay
+    from tiled_attention_attn_amd import _lib
+    from oracle import blockmask as OB
+    rp = Replay(("bwd", "blockmask"))
+    B, Hq, Hkv, N, D = 2, 2, 1, 520, 128
+    g = W.generator(13)
+    q, k, v, do = (W.randn_bf16(g, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D), (B, Hq, N, D)))
+    nt = (N + 127) // 128
+    tm = torch.stack([torch.stack([W.blockmask_tile_map(g, nt, 0.3) for _ in range(Hq)]) for _ in range(B)])
+    tm = tm.contiguous()
+    i32 = dict(dtype=torch.int32)
+    fwd_lists = [torch.zeros(B, Hq, nt, **i32), torch.zeros(B, Hq, nt, nt, **i32),
+                 torch.zeros(B, Hq, nt, **i32), torch.zeros(B, Hq, nt, nt, **i32)]
+    key_lists = [torch.zeros_like(x) for x in fwd_lists]
+    tmp = torch.zeros(B * Hq * nt * nt, dtype=torch.uint8)
+
+    def desc(ls):
+        return _lib.attn_blockmask(Bm=B, Hm=Hq, nQt=nt, nKt=nt, part_num=ls[0].data_ptr(), part_idx=ls[1].data_ptr(),
+                                   full_num=ls[2].data_ptr(), full_idx=ls[3].data_ptr())
+    bm, bm_t = desc(fwd_lists), desc(key_lists)
+    scale = 1.0 / math.sqrt(D)
+    mask = _lib.attn_mask_desc(flags=2, window_left=100, window_right=100)
+    mod = M.blockmask(tm.numpy(), 128, M.window(100, 100, N, N))
+    ro, rl = oracle.attention(*(x.to(torch.float64).numpy() for x in (q, k, v)), scale, mod)
+    o, lse = torch.from_numpy(ro).to(torch.bfloat16), torch.from_numpy(rl).to(torch.float32)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    ws = torch.zeros(max(int(rp.lib.attn_bwd_workspace_bytes(B, Hq, N)) // 4, 1))
+    rp.register(q=q, k=k, v=v, do=do, o=o, lse=lse, dq=dq, dk=dk, dv=dv, ws=ws, tm=tm, tmp=tmp,
+                **{f"lists{i}": t for i, t in enumerate(fwd_lists + key_lists)})
+    assert rp.lib.attn_build_blockmask(None, tm.data_ptr(), B, N, N, ctypes.byref(bm), None) == 0
+    assert rp.lib.attn_blockmask_transpose(ctypes.byref(bm), ctypes.byref(bm_t), tmp.data_ptr(), tmp.numel(),
+                                           None) == 0
+    rp.run()
+    st = rp.lib.attn_bwd_blockmask(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                                   o.data_ptr(), _strides(o), do.data_ptr(), _strides(do), lse.data_ptr(),
+                                   dq.data_ptr(), _strides(dq), dk.data_ptr(), _strides(dk), dv.data_ptr(),
+                                   _strides(dv), B, Hq, Hkv, N, N, D, 0, scale, ctypes.byref(mask), None,
+                                   ctypes.byref(bm), ctypes.byref(bm_t), ws.data_ptr(), ws.numel() * 4, None)
+    assert st == 0, st
+    rp.run(only=["bwd_pre", "bwd_kv"])
+    assert not rp.notes, rp.notes
+    for b in range(B):
+        for h in range(Hq):
+            pn, pi, fn, fi = OB.tile_lists(tm[b, h].numpy().T.copy())
+            got = [x[b, h].numpy() for x in key_lists]
+            assert all(np.array_equal(a, e) for a, e in zip(got, (pn, pi, fn, fi))), (b, h)
+    _, rk, rv, (_, mk, mv) = OBW.attention_bwd(*(x.to(torch.float64).numpy() for x in (q, k, v, do)), scale, mod,
+                                               row_block=256, bound=True, o_used=o.to(torch.float64).numpy())
+    _check_grad(dk, rk, mk, "dK")
+    _check_grad(dv, rv, mv, "dV")
+
+
 # ---- pins of the replay's own checks, on hand-written assembly ----------------------
 _ASM = """\
 probe:

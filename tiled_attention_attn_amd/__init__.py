@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     attn_decode_splitkv, attn_decode_combine, attn_decode_num_splits,
     attn_decode_noalloc, attn_decode_noalloc_max_bytes,
     attn_decode_ws_o_bytes, attn_decode_ws_lse_bytes, attn_bwd, attn_bwd_workspace_bytes,
+    attn_bwd_blockmask, attn_blockmask_transpose,
     attn_fwd_auto, attn_fwd_auto_plan, attn_auto_plan, PATH_PREFILL, PATH_SPLITKV,
     attn_probe_stream_read, attn_status_str, attn_abi_version,
     attn_mask_desc, attn_blockmask, lib_handle,

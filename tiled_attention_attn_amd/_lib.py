@@ -111,6 +111,9 @@ def declare_signatures(lib):
         "attn_bwd": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
                          I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
         "attn_bwd_workspace_bytes": (S, [I, I, I]),
+        "attn_bwd_blockmask": (I, [P, STR, P, STR, P, STR, P, STR, P, STR, P, P, STR, P, STR, P, STR,
+                                   I, I, I, I, I, I, I, F, MP, SP, BP, BP, P, S, P]),
+        "attn_blockmask_transpose": (I, [BP, BP, P, S, P]),
         "attn_fwd_auto_plan": (I, [I, I, I, I, I, I, SP, ctypes.POINTER(attn_auto_plan)]),
         "attn_fwd_auto": (I, [P, STR, P, STR, P, STR, P, STR, P, I, I, I, I, I, I, I, F, MP, SP, P, S, P]),
         "attn_probe_stream_read": (I, [P, S, I, P, P]),
@@ -136,7 +139,8 @@ EXPORTS = ("attn_fwd", "attn_fwd_blockmask", "attn_build_blockmask", "attn_block
            "attn_decode_splitkv", "attn_decode_combine", "attn_decode_noalloc",
            "attn_decode_noalloc_max_bytes", "attn_decode_ws_o_bytes",
            "attn_decode_ws_lse_bytes", "attn_decode_num_splits", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_fwd_auto_plan", "attn_fwd_auto",
+           "attn_bwd_workspace_bytes", "attn_bwd_blockmask", "attn_blockmask_transpose",
+           "attn_fwd_auto_plan", "attn_fwd_auto",
            "attn_probe_stream_read", "attn_status_str", "attn_abi_version")
 
 
@@ -380,6 +384,27 @@ class BlockMask:
         return s
 
 
+def attn_blockmask_transpose(bm: "BlockMask", stream=None) -> "BlockMask":
+    """The key-tile-major BlockMask of ``bm`` (a new BlockMask whose rows are key tiles), built on
+    the GPU by attn_blockmask_transpose; the backward pass over a BlockMask takes both."""
+    out = BlockMask.__new__(BlockMask)
+    out.Bm, out.Hm, out.nQt, out.nKt = bm.Bm, bm.Hm, bm.nKt, bm.nQt
+    dev = bm.part_num.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out.part_num = torch.zeros(bm.Bm, bm.Hm, out.nQt, **i32)
+    out.full_num = torch.zeros(bm.Bm, bm.Hm, out.nQt, **i32)
+    out.part_idx = torch.zeros(bm.Bm, bm.Hm, out.nQt, max(out.nKt, 1), **i32)
+    out.full_idx = torch.zeros(bm.Bm, bm.Hm, out.nQt, max(out.nKt, 1), **i32)
+    tmp = torch.empty(max(bm.Bm * bm.Hm * bm.nQt * bm.nKt, 1), dtype=torch.uint8, device=dev)
+    _on_device(("part_num", bm.part_num), ("out", out.part_num), ("tmp", tmp))
+    s_in, s_out = bm.struct(), out.struct()
+    _check("attn_blockmask_transpose",
+           _lib.attn_blockmask_transpose(ctypes.byref(s_in), ctypes.byref(s_out), _ptr(tmp),
+                                         tmp.numel(), _stream(stream)))
+    out._tmp = tmp  # the map is overwritten by the kernel; kept alive until the stream uses it
+    return out
+
+
 def attn_blockmask_bytes(Bm, Hm, nQt, nKt):
     return int(_lib.attn_blockmask_bytes(Bm, Hm, nQt, nKt))
 
@@ -580,6 +605,40 @@ def attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace=None, scale=None, mask=
                        B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, sp, _ptr(workspace), workspace.numel() * 4,
                        _stream(stream))
     _check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_blockmask(q, k, v, o, d_o, lse, dq, dk, dv, bm: "BlockMask", bm_t: "BlockMask",
+                       workspace=None, scale=None, mask=None, stream=None, smod=None):
+    """dQ, dK, dV of attn_fwd_blockmask's O: ``bm`` the forward BlockMask, ``bm_t`` its
+    key-tile-major lists (attn_blockmask_transpose(bm)); otherwise as attn_bwd."""
+    dt = _half(q, k, v, o, d_o, dq, dk, dv)
+    B, Hq, Hkv, Nq, Nk, D = _check_qkvo(q, k, v, o)
+    for name, t, want in (("d_o", d_o, q.shape), ("dq", dq, q.shape), ("dk", dk, k.shape),
+                          ("dv", dv, k.shape)):
+        _shape(name, t, want)
+    if lse is None:
+        raise TypeError("lse (the forward pass's float32 [B, Hq, Nq]) is required")
+    _check_lse(lse, B, Hq, Nq)
+    _on_device(("q", q), ("k", k), ("v", v), ("o", o), ("d_o", d_o), ("lse", lse), ("dq", dq),
+               ("dk", dk), ("dv", dv), ("workspace", workspace), ("bm", bm.part_num),
+               ("bm_t", bm_t.part_num), *_mask_tensors(mask, B), *_smod_tensors(smod, Hq))
+    need = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise TypeError("workspace must be contiguous float32")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    keep, mp = _mask_ptr(mask)
+    keep_s, sp = _smod_ptr(smod)
+    s1, s2 = bm.struct(), bm_t.struct()
+    st = _lib.attn_bwd_blockmask(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                 _ptr(o), _strides(o), _ptr(d_o), _strides(d_o), _ptr(lse),
+                                 _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                                 B, Hq, Hkv, Nq, Nk, D, dt, scale, mp, sp, ctypes.byref(s1),
+                                 ctypes.byref(s2), _ptr(workspace), workspace.numel() * 4,
+                                 _stream(stream))
+    _check("attn_bwd_blockmask", st)
     return dq, dk, dv
 
 

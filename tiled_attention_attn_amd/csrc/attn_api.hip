@@ -14,7 +14,8 @@ int launch_decode(const DecParams& p, int D, int dtype, hipStream_t stream);
 int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq, int S, int D,
                    int dtype, void* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
                    hipStream_t stream);
-int launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t stream);
+int launch_bwd(const BwdParams& p, int D, int dtype, bool blockmask, hipStream_t stream);
+int launch_blockmask_transpose(const BmTransposeParams& p, hipStream_t stream);
 }  // namespace tattn
 
 using namespace tattn;
@@ -192,9 +193,115 @@ AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_sco
 
 }  // namespace
 
+namespace {
+
+int bwd_impl(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
+             const void* v, const int64_t v_stride[3], const void* o, const int64_t o_stride[3],
+             const void* d_o, const int64_t do_stride[3], const float* lse, void* dq,
+             const int64_t dq_stride[3], void* dk, const int64_t dk_stride[3], void* dv,
+             const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
+             int dtype, float scale, const attn_mask_desc* mask, const attn_score_mod* smod,
+             float* workspace, size_t workspace_bytes, const attn_blockmask* bm,
+             const attn_blockmask* bm_t, hipStream_t stream) {
+  // Tensors without rows may be NULL (an empty tensor has no storage).
+  if (Nq > 0 && (!q || !o || !d_o || !dq || !lse)) return ATTN_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+  if (!workspace && Nq > 0) return ATTN_ERR_NULL;
+  const int64_t* all[8] = {q_stride, k_stride, v_stride, o_stride, do_stride, dq_stride, dk_stride,
+                           dv_stride};
+  int st;
+  for (const int64_t* s : all)
+    if ((st = check_strides(s))) return st;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if ((st = check_dtype(dtype))) return st;
+  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
+  const void* ptrs[9] = {q, k, v, o, d_o, dq, dk, dv, workspace};
+  for (const void* x : ptrs)
+    if (x && !aligned16(x)) return ATTN_ERR_ALIGN;
+  // K / V tiles (dQ kernel) and Q / dO tiles (dK / dV kernel) are streamed
+  // with 32-bit byte offsets.
+  if (k_stride[2] >= kMaxRowStride || v_stride[2] >= kMaxRowStride ||
+      q_stride[2] >= kMaxRowStride || do_stride[2] >= kMaxRowStride)
+    return ATTN_ERR_STRIDE;
+  if ((st = check_scale(scale))) return st;
+  if (bm != nullptr) {
+    // the forward lists (dQ) and their key-tile-major transpose (dK / dV)
+    if (bm_t == nullptr) return ATTN_ERR_NULL;
+    if (!bm->part_num || !bm->part_idx || !bm->full_num || !bm->full_idx || !bm_t->part_num ||
+        !bm_t->part_idx || !bm_t->full_num || !bm_t->full_idx)
+      return ATTN_ERR_NULL;
+    if (bm->nQt != (Nq + 127) / 128 || bm->nKt != (Nk + 127) / 128) return ATTN_ERR_BLOCKMASK;
+    if (!(bm->Bm == 1 || bm->Bm == B) || !(bm->Hm == 1 || bm->Hm == Hq)) return ATTN_ERR_BLOCKMASK;
+    if (bm_t->Bm != bm->Bm || bm_t->Hm != bm->Hm || bm_t->nQt != bm->nKt || bm_t->nKt != bm->nQt)
+      return ATTN_ERR_BLOCKMASK;
+  }
+  BwdParams p;
+  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
+  if ((st = make_smod(smod, scale, Hq / Hkv, p.smod))) return st;
+  // The BlockMask backward kernels take no score change.
+  if (bm != nullptr && p.smod.flags != 0) return ATTN_ERR_SCORE_MOD;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = d_o;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
+  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
+  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
+  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
+  p.do_sb = do_stride[0]; p.do_sh = do_stride[1]; p.do_sn = do_stride[2];
+  p.dq_sb = dq_stride[0]; p.dq_sh = dq_stride[1]; p.dq_sn = dq_stride[2];
+  p.dk_sb = dk_stride[0]; p.dk_sh = dk_stride[1]; p.dk_sn = dk_stride[2];
+  p.dv_sb = dv_stride[0]; p.dv_sh = dv_stride[1]; p.dv_sn = dv_stride[2];
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Nq = Nq; p.Nk = Nk;
+  p.nq_pad = (Nq + 63) / 64 * 64;
+  p.c2 = scale * 1.4426950408889634f;
+  p.scale = scale;
+  p.ws_l2 = workspace;
+  p.ws_delta = workspace + (size_t)B * Hq * p.nq_pad;
+  // Causal-like masks give later query tiles more keys and earlier key tiles
+  // more rows: pair tile i with n-1-i in both kernels.
+  // BlockMask lists are paired like the forward BlockMask kernel's.
+  const bool pair = (bm != nullptr || causal_like(p.mask)) && !(p.sched & ATTN_SCHED_NO_PAIRING);
+  const bool remap = !(p.sched & ATTN_SCHED_NO_XCD_REMAP);
+  p.n_kt = (Nk + 127) / 128;
+  p.kv_paired = pair && p.n_kt > 1;
+  p.kv_slots = p.kv_paired ? (p.n_kt + 1) / 2 : p.n_kt;
+  p.kv_xcd_remap = remap && ((long)B * Hkv * p.kv_slots) % 8 == 0;
+  p.n_qt = (Nq + 127) / 128;
+  p.q_paired = pair && p.n_qt > 1;
+  p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
+  p.q_xcd_remap = remap && ((long)B * Hq * p.q_slots) % 8 == 0;
+  // dQ groups B Hq n_qt, dK/dV groups B Hkv n_kt, Delta threads 8 per padded row
+  if (!grid_fits((int64_t)B * Hq * p.n_qt) || !grid_fits((int64_t)B * Hkv * p.n_kt) ||
+      !grid_fits(((int64_t)B * Hq * p.nq_pad * 8 + 255) / 256))
+    return ATTN_ERR_SHAPE;
+  p.bm_B = bm ? bm->Bm : 1;
+  p.bm_H = bm ? bm->Hm : 1;
+  p.part_num = bm ? bm->part_num : nullptr;
+  p.part_idx = bm ? bm->part_idx : nullptr;
+  p.full_num = bm ? bm->full_num : nullptr;
+  p.full_idx = bm ? bm->full_idx : nullptr;
+  p.tpart_num = bm ? bm_t->part_num : nullptr;
+  p.tpart_idx = bm ? bm_t->part_idx : nullptr;
+  p.tfull_num = bm ? bm_t->full_num : nullptr;
+  p.tfull_idx = bm ? bm_t->full_idx : nullptr;
+  return launch_bwd(p, D, dtype, bm != nullptr, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
-int attn_abi_version(void) { return 7; }
+int attn_abi_version(void) { return 8; }
 
 const char* attn_status_str(int status) {
   switch (status) {
@@ -460,74 +567,58 @@ int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int6
              const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
              int dtype, float scale, const attn_mask_desc* mask, const attn_score_mod* smod,
              float* workspace, size_t workspace_bytes, hipStream_t stream) {
-  // Tensors without rows may be NULL (an empty tensor has no storage).
-  if (Nq > 0 && (!q || !o || !d_o || !dq || !lse)) return ATTN_ERR_NULL;
-  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
-  if (!workspace && Nq > 0) return ATTN_ERR_NULL;
-  const int64_t* all[8] = {q_stride, k_stride, v_stride, o_stride, do_stride, dq_stride, dk_stride,
-                           dv_stride};
-  int st;
-  for (const int64_t* s : all)
-    if ((st = check_strides(s))) return st;
-  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (Nq > kMaxLen || Nk > kMaxLen || B > 65535 || Hq > 65535) return ATTN_ERR_SHAPE;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if ((st = check_dtype(dtype))) return st;
-  if (Hkv == 0 || Hq == 0 || Hq % Hkv != 0) return ATTN_ERR_GQA;
-  const void* ptrs[9] = {q, k, v, o, d_o, dq, dk, dv, workspace};
-  for (const void* x : ptrs)
-    if (x && !aligned16(x)) return ATTN_ERR_ALIGN;
-  // K / V tiles (dQ kernel) and Q / dO tiles (dK / dV kernel) are streamed
-  // with 32-bit byte offsets.
-  if (k_stride[2] >= kMaxRowStride || v_stride[2] >= kMaxRowStride ||
-      q_stride[2] >= kMaxRowStride || do_stride[2] >= kMaxRowStride)
-    return ATTN_ERR_STRIDE;
-  if ((st = check_scale(scale))) return st;
-  BwdParams p;
-  if ((st = make_mask(mask, Nq, Nk, true, p.mask, &p.sched))) return st;
-  if ((st = make_smod(smod, scale, Hq / Hkv, p.smod))) return st;
-  if (workspace_bytes < attn_bwd_workspace_bytes(B, Hq, Nq)) return ATTN_ERR_WORKSPACE;
-  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = o;
-  p.dout = d_o;
-  p.lse = lse;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.q_sb = q_stride[0]; p.q_sh = q_stride[1]; p.q_sn = q_stride[2];
-  p.k_sb = k_stride[0]; p.k_sh = k_stride[1]; p.k_sn = k_stride[2];
-  p.v_sb = v_stride[0]; p.v_sh = v_stride[1]; p.v_sn = v_stride[2];
-  p.o_sb = o_stride[0]; p.o_sh = o_stride[1]; p.o_sn = o_stride[2];
-  p.do_sb = do_stride[0]; p.do_sh = do_stride[1]; p.do_sn = do_stride[2];
-  p.dq_sb = dq_stride[0]; p.dq_sh = dq_stride[1]; p.dq_sn = dq_stride[2];
-  p.dk_sb = dk_stride[0]; p.dk_sh = dk_stride[1]; p.dk_sn = dk_stride[2];
-  p.dv_sb = dv_stride[0]; p.dv_sh = dv_stride[1]; p.dv_sn = dv_stride[2];
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.Nq = Nq; p.Nk = Nk;
-  p.nq_pad = (Nq + 63) / 64 * 64;
-  p.c2 = scale * 1.4426950408889634f;
-  p.scale = scale;
-  p.ws_l2 = workspace;
-  p.ws_delta = workspace + (size_t)B * Hq * p.nq_pad;
-  // Causal-like masks give later query tiles more keys and earlier key tiles
-  // more rows: pair tile i with n-1-i in both kernels.
-  const bool pair = causal_like(p.mask) && !(p.sched & ATTN_SCHED_NO_PAIRING);
-  const bool remap = !(p.sched & ATTN_SCHED_NO_XCD_REMAP);
-  p.n_kt = (Nk + 127) / 128;
-  p.kv_paired = pair && p.n_kt > 1;
-  p.kv_slots = p.kv_paired ? (p.n_kt + 1) / 2 : p.n_kt;
-  p.kv_xcd_remap = remap && ((long)B * Hkv * p.kv_slots) % 8 == 0;
-  p.n_qt = (Nq + 127) / 128;
-  p.q_paired = pair && p.n_qt > 1;
-  p.q_slots = p.q_paired ? (p.n_qt + 1) / 2 : p.n_qt;
-  p.q_xcd_remap = remap && ((long)B * Hq * p.q_slots) % 8 == 0;
-  // dQ groups B Hq n_qt, dK/dV groups B Hkv n_kt, Delta threads 8 per padded row
-  if (!grid_fits((int64_t)B * Hq * p.n_qt) || !grid_fits((int64_t)B * Hkv * p.n_kt) ||
-      !grid_fits(((int64_t)B * Hq * p.nq_pad * 8 + 255) / 256))
-    return ATTN_ERR_SHAPE;
-  return launch_bwd(p, D, dtype, stream);
+  return bwd_impl(q, q_stride, k, k_stride, v, v_stride, o, o_stride, d_o, do_stride, lse, dq,
+                  dq_stride, dk, dk_stride, dv, dv_stride, B, Hq, Hkv, Nq, Nk, D, dtype, scale,
+                  mask, smod, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+int attn_bwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
+                       const int64_t k_stride[3], const void* v, const int64_t v_stride[3],
+                       const void* o, const int64_t o_stride[3], const void* d_o,
+                       const int64_t do_stride[3], const float* lse, void* dq,
+                       const int64_t dq_stride[3], void* dk, const int64_t dk_stride[3], void* dv,
+                       const int64_t dv_stride[3], int B, int Hq, int Hkv, int Nq, int Nk, int D,
+                       int dtype, float scale, const attn_mask_desc* mask,
+                       const attn_score_mod* smod, const attn_blockmask* bm,
+                       const attn_blockmask* bm_t, float* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (bm == nullptr || bm_t == nullptr) return ATTN_ERR_NULL;
+  return bwd_impl(q, q_stride, k, k_stride, v, v_stride, o, o_stride, d_o, do_stride, lse, dq,
+                  dq_stride, dk, dk_stride, dv, dv_stride, B, Hq, Hkv, Nq, Nk, D, dtype, scale,
+                  mask, smod, workspace, workspace_bytes, bm, bm_t, stream);
+}
+
+int attn_blockmask_transpose(const attn_blockmask* bm, attn_blockmask* out, uint8_t* map_tmp,
+                             size_t map_tmp_bytes, hipStream_t stream) {
+  if (bm == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (!bm->part_num || !bm->part_idx || !bm->full_num || !bm->full_idx || !out->part_num ||
+      !out->part_idx || !out->full_num || !out->full_idx)
+    return ATTN_ERR_NULL;
+  if (bm->Bm < 1 || bm->Hm < 1 || bm->Bm > 65535 || bm->Hm > 65535) return ATTN_ERR_BLOCKMASK;
+  if (bm->nQt < 0 || bm->nKt < 0 || bm->nQt > (kMaxLen + 127) / 128 ||
+      bm->nKt > (kMaxLen + 127) / 128)
+    return ATTN_ERR_BLOCKMASK;
+  if (out->Bm != bm->Bm || out->Hm != bm->Hm || out->nQt != bm->nKt || out->nKt != bm->nQt)
+    return ATTN_ERR_BLOCKMASK;
+  const size_t need = (size_t)bm->Bm * bm->Hm * bm->nQt * bm->nKt;
+  if (need == 0) return ATTN_OK;
+  if (map_tmp == nullptr) return ATTN_ERR_NULL;
+  if (map_tmp_bytes < need) return ATTN_ERR_WORKSPACE;
+  BmTransposeParams tp{bm->part_num, bm->part_idx, bm->full_num, bm->full_idx,
+                       bm->Bm, bm->Hm, bm->nQt, bm->nKt, map_tmp};
+  int st = launch_blockmask_transpose(tp, stream);
+  if (st) return st;
+  // the key-tile-major map compacted into lists by the builder (its map path)
+  BmBuildParams p;
+  p.mask = MaskParams{0u, -1, -1, 1, nullptr, 1, 2};
+  p.tile_map = map_tmp;
+  p.Nq = bm->nKt * 128;
+  p.Nk = bm->nQt * 128;
+  p.shift = 0;
+  p.Bm = bm->Bm; p.Hm = bm->Hm; p.nQt = bm->nKt; p.nKt = bm->nQt;
+  p.part_num = out->part_num; p.part_idx = out->part_idx;
+  p.full_num = out->full_num; p.full_idx = out->full_idx;
+  return launch_blockmask(p, stream);
 }
 
 }  // extern "C"

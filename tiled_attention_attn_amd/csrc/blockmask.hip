@@ -78,6 +78,40 @@ __global__ void __launch_bounds__(256) blockmask_kernel(const BmBuildParams p) {
   }
 }
 
+// Key-tile-major class map of a BlockMask: map_t[b][h][kt][qt] = the class of
+// tile (qt, kt) in the lists (binary search in the ascending FULL and PARTIAL
+// lists of row qt).  Every entry is written, so the map needs no clearing.
+// One work group per (batch row, head, query tile); a thread per key tile.
+__global__ void __launch_bounds__(256) blockmask_transpose_kernel(const BmTransposeParams p) {
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t row = ((int64_t)b * p.Hm + h) * p.nQt + qt;
+  const int nf = p.full_num[row], np = p.part_num[row];
+  const int32_t* fi = p.full_idx + row * p.nKt;
+  const int32_t* pi = p.part_idx + row * p.nKt;
+  auto in_list = [](const int32_t* a, int n, int key) {
+    int lo = 0, hi = n - 1;
+    while (lo <= hi) {
+      const int mid = (lo + hi) >> 1;
+      const int v = a[mid];
+      if (v == key) return true;
+      if (v < key) lo = mid + 1; else hi = mid - 1;
+    }
+    return false;
+  };
+  uint8_t* dst = p.map_t + ((int64_t)b * p.Hm + h) * p.nKt * p.nQt + qt;
+  for (int kt = threadIdx.x; kt < p.nKt; kt += 256) {
+    const int c = in_list(fi, nf, kt) ? ATTN_TILE_FULL
+                                      : (in_list(pi, np, kt) ? ATTN_TILE_PARTIAL : ATTN_TILE_EMPTY);
+    dst[(int64_t)kt * p.nQt] = (uint8_t)c;
+  }
+}
+
+int launch_blockmask_transpose(const BmTransposeParams& p, hipStream_t stream) {
+  dim3 grid(p.nQt, p.Hm, p.Bm), block(256);
+  hipLaunchKernelGGL(blockmask_transpose_kernel, grid, block, 0, stream, p);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 int launch_blockmask(const BmBuildParams& p, hipStream_t stream) {
   dim3 grid(p.nQt, p.Hm, p.Bm), block(256);
   hipLaunchKernelGGL(blockmask_kernel, grid, block, 0, stream, p);

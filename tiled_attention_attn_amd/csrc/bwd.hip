@@ -169,7 +169,11 @@ template <int D> struct BwdQRows { static constexpr int value = D == 64 ? 64 : 3
 // G (2R + 1) <= 8192 (the host checks it).
 constexpr int kMaxRelTables = 8192;
 
-template <int D, typename T, bool SM>
+// BlockMask (BM): the dK / dV kernel walks the key tile's column of the
+// BlockMask -- for each query head of the KV head, its FULL then PARTIAL query
+// tiles from the key-tile-major (transposed) lists -- in QB-row steps; a FULL
+// tile applies no predicate, a PARTIAL tile the mask intervals.
+template <int D, typename T, bool SM, bool BM>
 __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem, int kt, int b,
                                         int kvh) {
   constexpr int QB = BwdQRows<D>::value;
@@ -236,19 +240,78 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 
   // Rows the tile's keys see: from the first key's first row to the last
   // key's last row (both ends never decrease with the key).
-  int n_qs = 0, qs0 = 0;
-  if (p.Nk > k0) {
-    int a0, b0, a1, b1;
-    key_rows(p.mask, b, k0, p.Nq, p.Nk, shift, a0, b0);
-    key_rows(p.mask, b, min(k0 + 127, p.Nk - 1), p.Nq, p.Nk, shift, a1, b1);
-    if (b1 >= a0) {
-      qs0 = (a0 / QB) * QB;
-      n_qs = (b1 + 1 - qs0 + QB - 1) / QB;
+  // ---- step sequence ----
+  // Dense masks: for g < G, query blocks qs0 + qi QB (qi < n_qs), from the
+  // first key's first row to the last key's last row.  BlockMask: for g < G,
+  // the FULL then PARTIAL query tiles of head kvh G + g, SPQ blocks each.
+  constexpr int SPQ = 128 / QB;  // steps per 128-row BlockMask tile
+  int n_qs = 0, qs0 = 0, n_steps = 0;
+  if constexpr (!BM) {
+    if (p.Nk > k0) {
+      int a0, b0, a1, b1;
+      key_rows(p.mask, b, k0, p.Nq, p.Nk, shift, a0, b0);
+      key_rows(p.mask, b, min(k0 + 127, p.Nk - 1), p.Nq, p.Nk, shift, a1, b1);
+      if (b1 >= a0) {
+        qs0 = (a0 / QB) * QB;
+        n_qs = (b1 + 1 - qs0 + QB - 1) / QB;
+      }
+    }
+    n_qs = __builtin_amdgcn_readfirstlane(n_qs);
+    qs0 = __builtin_amdgcn_readfirstlane(qs0);
+    n_steps = p.G * n_qs;
+  }
+  // Transposed-list row of head kvh G + g for this key tile.
+  auto bm_row = [&](int g) -> int64_t {
+    const int hh = p.bm_H > 1 ? kvh * p.G + g : 0, bb = p.bm_B > 1 ? b : 0;
+    return ((int64_t)bb * p.bm_H + hh) * p.n_kt + kt;
+  };
+  if constexpr (BM) {
+    for (int g = 0; g < p.G; ++g) {
+      const int64_t r = bm_row(g);
+      n_steps += SPQ * (p.tfull_num[r] + p.tpart_num[r]);
     }
   }
-  n_qs = __builtin_amdgcn_readfirstlane(n_qs);
-  qs0 = __builtin_amdgcn_readfirstlane(qs0);
-  const int n_steps = p.G * n_qs;
+  // A cursor over the step sequence: head g, block or tile index i, sub-step
+  // sub, and (BlockMask) the head's tile count nt and FULL count nf.
+  struct Cur { int g, i, sub, nt, nf; };
+  auto cur_head = [&](Cur& c) {  // BlockMask: first head at or after c.g with a tile
+    for (; c.g < p.G; ++c.g) {
+      const int64_t r = bm_row(c.g);
+      c.nf = p.tfull_num[r];
+      c.nt = c.nf + p.tpart_num[r];
+      if (c.nt > 0) break;
+    }
+  };
+  auto cur_init = [&](Cur& c) {
+    c = Cur{0, 0, 0, 0, 0};
+    if constexpr (BM) cur_head(c);
+  };
+  // First row of the cursor's step; `partial`: apply the mask intervals.
+  auto cur_q0 = [&](const Cur& c, bool& partial) -> int {
+    if constexpr (!BM) {
+      partial = true;
+      return qs0 + c.i * QB;
+    } else {
+      const int64_t base = bm_row(c.g) * p.n_qt;
+      partial = c.i >= c.nf;
+      const int qt = partial ? p.tpart_idx[base + c.i - c.nf] : p.tfull_idx[base + c.i];
+      return qt * 128 + c.sub * QB;
+    }
+  };
+  auto cur_next = [&](Cur& c) {
+    if constexpr (!BM) {
+      if (++c.i == n_qs) { c.i = 0; ++c.g; }
+    } else {
+      if (++c.sub == SPQ) {
+        c.sub = 0;
+        if (++c.i == c.nt) {
+          c.i = 0;
+          ++c.g;
+          cur_head(c);
+        }
+      }
+    }
+  };
 
   // Copies: lane slot (inst*64 + lane) of a tile is row r, 16-byte chunk
   // ch ^ swz(r), as for the forward kernel's K/V tiles.
@@ -284,15 +347,22 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
         }
   }
 
-  // Steps run head-major: (g, qi) for g < G, qi < n_qs; a cursor per
-  // direction (copies issued, steps computed) advances without divisions.
+  // Steps run head-major; a cursor per direction (copies issued, steps
+  // computed) advances without divisions.
   const T* q_head = static_cast<const T*>(p.q) + b * p.q_sb + (int64_t)kvh * p.G * p.q_sh;
   const T* do_head = static_cast<const T*>(p.dout) + b * p.do_sb + (int64_t)kvh * p.G * p.do_sh;
   const float* ws_head = p.ws_l2 + (int64_t)(b * p.Hq + kvh * p.G) * p.nq_pad;
   const int64_t ws_delta_off = p.ws_delta - p.ws_l2;
-  int ld_g = 0, ld_qi = 0;
+  Cur ld;
+  cur_init(ld);
+  // The last QB-row block that holds a row: a BlockMask step past the last
+  // row (the tail of a ragged last tile) copies that block instead and
+  // computes nothing.
+  const int last_q0 = p.Nq > 0 ? ((p.Nq - 1) / QB) * QB : 0;
   auto load_next = [&](int stage) {
-    const int q0 = qs0 + ld_qi * QB;
+    bool partial_unused;
+    const int q0 = min(cur_q0(ld, partial_unused), last_q0);
+    const int ld_g = ld.g;
     const uint32_t lb = lds_addr(smem) + stage * STAGE_BYTES;
     const T* qbase = q_head + ld_g * p.q_sh + (int64_t)q0 * p.q_sn;
     const T* dbase = do_head + ld_g * p.do_sh + (int64_t)q0 * p.do_sn;
@@ -321,24 +391,28 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
                          4 * (li % (QB / 4));
       dma16(src, lb + LD_OFF);
     }
-    if (++ld_qi == n_qs) { ld_qi = 0; ++ld_g; }
+    cur_next(ld);
   };
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d) dk[d] = dv[d] = f32x16{};
 
-  int qi = 0, gcur = 0;
+  Cur cc;
+  cur_init(cc);
   auto step = [&](auto stc, int s) {
     constexpr int ST = decltype(stc)::value;
     wait_vmem();
     lds_barrier();
     if (s + 1 < n_steps) load_next(ST ^ 1);
-    const int q0 = qs0 + qi * QB;
-    const int g = gcur;
-    if (++qi == n_qs) { qi = 0; ++gcur; }
-    if (q0 > w_hi || q0 + QB - 1 < w_lo) return;  // no key of this wave is seen by these rows
-    const bool full = w_lo_max <= q0 && w_hi_min >= q0 + QB - 1;
+    bool partial;
+    const int q0 = cur_q0(cc, partial);
+    const int g = cc.g;
+    cur_next(cc);
+    if (q0 >= p.Nq) return;  // tail of a ragged last BlockMask tile
+    // rows outside the wave's keys' rows (only where the mask intervals apply)
+    if (partial && (q0 > w_hi || q0 + QB - 1 < w_lo)) return;
+    const bool full = !partial || (w_lo_max <= q0 && w_hi_min >= q0 + QB - 1);
     const TATTN_LDS char* tQ = smem + ST * STAGE_BYTES;
     const TATTN_LDS char* tD = tQ + TILE_BYTES;
     const TATTN_LDS float* tL = reinterpret_cast<const TATTN_LDS float*>(tQ + LD_OFF);
@@ -458,7 +532,7 @@ __device__ __forceinline__ void kv_tile(const BwdParams& p, TATTN_LDS char* smem
 // 512-entry register file of one SIMD lane.
 template <int D> struct BwdKvOcc { static constexpr int value = D == 64 ? 2 : 1; };
 
-template <int D, typename T, bool SM>
+template <int D, typename T, bool SM, bool BM>
 __global__ void __launch_bounds__(kBwdThreads)
 __attribute__((amdgpu_waves_per_eu(BwdKvOcc<D>::value, BwdKvOcc<D>::value)))
 bwd_kv_kernel(const BwdParams p) {
@@ -478,12 +552,12 @@ bwd_kv_kernel(const BwdParams p) {
   const int slot = unit % p.kv_slots;
   const int r = unit / p.kv_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
-  kv_tile<D, T, SM>(p, smem, slot, b, kvh);
+  kv_tile<D, T, SM, BM>(p, smem, slot, b, kvh);
   if (p.kv_paired) {
     const int kt2 = p.n_kt - 1 - slot;
     if (kt2 != slot) {
       __syncthreads();
-      kv_tile<D, T, SM>(p, smem, kt2, b, kvh);
+      kv_tile<D, T, SM, BM>(p, smem, kt2, b, kvh);
     }
   }
 }
@@ -492,7 +566,9 @@ bwd_kv_kernel(const BwdParams p) {
 // Keys per step as in the forward kernel: 128 at D=64, 64 at D=128.
 template <int D> struct BwdKBlk { static constexpr int value = D == 64 ? 128 : 64; };
 
-template <int D, typename T, bool SM>
+// BlockMask (BM): the query tile's FULL then PARTIAL key tiles of the
+// forward lists, kKBlk keys a step, as in the forward kernel.
+template <int D, typename T, bool SM, bool BM>
 __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem, int qt, int b,
                                        int h, int kvh) {
   constexpr int kKBlk = BwdKBlk<D>::value;
@@ -541,8 +617,11 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
     hd.tab = tab;
     if (p.smod.flags & ATTN_SCORE_REL_BIAS) stage_rel_table(p.smod, h, tab, tid, kBwdThreads);
   }
+  constexpr int SPT = 128 / kKBlk;  // steps per 128-key BlockMask tile
   int n_steps = 0, kb_begin = 0, lo_last = 0, hi_first = 0;
-  {
+  int64_t bm_base = 0;
+  int bm_nf = 0;
+  if constexpr (!BM) {
     int lo_first, hi_last, t0;
     const int last_row = min(q0 + 128, p.Nq) - 1;
     row_interval(p.mask, b, q0 + shift, p.Nk, lo_first, hi_first);
@@ -552,7 +631,32 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
       kb_begin = (lo_first / kKBlk) * kKBlk;
       n_steps = (hi_last + 1 - kb_begin + kKBlk - 1) / kKBlk;
     }
+  } else {
+    const int bb = p.bm_B > 1 ? b : 0, hh = p.bm_H > 1 ? h : 0;
+    const int64_t row = ((int64_t)bb * p.bm_H + hh) * p.n_qt + qt;
+    bm_nf = p.full_num[row];
+    n_steps = SPT * (bm_nf + p.part_num[row]);
+    bm_base = row * p.n_kt;
   }
+  // First key of step s and whether it applies the row's mask interval
+  // (dense masks: wherever a step is not inside every row's interval;
+  // BlockMask: on PARTIAL tiles, and [0, Nk) on a ragged last tile).
+  auto step_kb = [&](int s, bool& masked, bool& use_row) -> int {
+    if constexpr (!BM) {
+      const int kb = kb_begin + s * kKBlk;
+      masked = !(kb >= lo_last && kb + kKBlk - 1 <= hi_first && kb + kKBlk <= p.Nk);
+      use_row = true;
+      return kb;
+    } else {
+      const int t = s / SPT;
+      const bool partial = t >= bm_nf;
+      const int kt = partial ? p.part_idx[bm_base + t - bm_nf] : p.full_idx[bm_base + t];
+      const int kb = kt * 128 + (s % SPT) * kKBlk;
+      use_row = partial;
+      masked = partial || kb + kKBlk > p.Nk;
+      return kb;
+    }
+  };
 
   uint32_t dma_row[PER_WAVE], kvoff[PER_WAVE], vvoff[PER_WAVE], dma_lds[PER_WAVE];
 #pragma unroll
@@ -587,7 +691,9 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
   const T* Kbh = static_cast<const T*>(p.k) + b * p.k_sb + kvh * p.k_sh;
   const T* Vbh = static_cast<const T*>(p.v) + b * p.v_sb + kvh * p.v_sh;
   auto load_step = [&](int s, int stage) {
-    const int kb = kb_begin + s * kKBlk;
+    bool m_unused, u_unused;
+    int kb = step_kb(s, m_unused, u_unused);
+    kb = kb > p.Nk - 1 ? p.Nk - 1 : kb;  // the tail of a ragged last BlockMask tile
     const uint32_t lk = lds_addr(smem) + stage * STAGE_BYTES;
     const T* kbase = Kbh + (int64_t)kb * p.k_sn;
     const T* vbase = Vbh + (int64_t)kb * p.v_sn;
@@ -617,13 +723,15 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
     wait_vmem();
     lds_barrier();
     if (s + 1 < n_steps) load_step(s + 1, ST ^ 1);
-    const int kb = kb_begin + s * kKBlk;
-    const bool masked = !(kb >= lo_last && kb + kKBlk - 1 <= hi_first && kb + kKBlk <= p.Nk);
+    bool masked, use_row;
+    const int kb = step_kb(s, masked, use_row);
+    if (kb >= p.Nk) return;  // tail of a ragged last BlockMask tile
     const TATTN_LDS char* tK = smem + ST * STAGE_BYTES;
     const TATTN_LDS char* tV = tK + TILE_BYTES;
-    const uint32_t base = (uint32_t)(kb + 4 * half - lo);
-    const uint32_t width = hi >= lo ? (uint32_t)(hi - lo) : 0u;
-    const uint32_t base_ok = hi >= lo ? base : 0x80000000u;
+    const int lo_m = use_row ? lo : 0, hi_m = use_row ? hi : p.Nk - 1;
+    const uint32_t base = (uint32_t)(kb + 4 * half - lo_m);
+    const uint32_t width = hi_m >= lo_m ? (uint32_t)(hi_m - lo_m) : 0u;
+    const uint32_t base_ok = hi_m >= lo_m ? base : 0x80000000u;
 #pragma unroll
     for (int kbk = 0; kbk < NKB; ++kbk) {
       // ---- S^T = K Q^T and dP^T = V dO^T for 32 keys ----
@@ -701,7 +809,7 @@ __device__ __forceinline__ void q_tile(const BwdParams& p, TATTN_LDS char* smem,
   }
 }
 
-template <int D, typename T, bool SM>
+template <int D, typename T, bool SM, bool BM>
 __global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_q_kernel(const BwdParams p) {
   // the ring (64 KB), then the head's bias table (8 KB) when SM
@@ -723,41 +831,52 @@ bwd_q_kernel(const BwdParams p) {
   r /= p.q_slots;
   const int kvh = r % p.Hkv, b = r / p.Hkv;
   const int h = kvh * p.G + g;
-  q_tile<D, T, SM>(p, smem, slot, b, h, kvh);
+  q_tile<D, T, SM, BM>(p, smem, slot, b, h, kvh);
   if (p.q_paired) {
     const int qt2 = p.n_qt - 1 - slot;
     if (qt2 != slot) {
       __syncthreads();
-      q_tile<D, T, SM>(p, smem, qt2, b, h, kvh);
+      q_tile<D, T, SM, BM>(p, smem, qt2, b, h, kvh);
     }
   }
 }
 
-template <int D, typename T>
+template <int D, typename T, bool BM>
 void launch_bwd_t(const BwdParams& p, dim3 gpre, dim3 gkv, dim3 gq, dim3 block, hipStream_t stream) {
   if (gpre.x) hipLaunchKernelGGL((bwd_pre_kernel<D, T>), gpre, block, 0, stream, p);
-  if (p.smod.flags) {
-    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, true>), gkv, block, 0, stream, p);
-    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, true>), gq, block, 0, stream, p);
+  if constexpr (BM) {  // no score change over a BlockMask (the host rejects it)
+    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, false, true>), gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, false, true>), gq, block, 0, stream, p);
+  } else if (p.smod.flags) {
+    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, true, BM>), gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, true, BM>), gq, block, 0, stream, p);
   } else {
-    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, false>), gkv, block, 0, stream, p);
-    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, false>), gq, block, 0, stream, p);
+    if (gkv.x) hipLaunchKernelGGL((bwd_kv_kernel<D, T, false, BM>), gkv, block, 0, stream, p);
+    if (gq.x) hipLaunchKernelGGL((bwd_q_kernel<D, T, false, BM>), gq, block, 0, stream, p);
   }
 }
 
-int launch_bwd(const BwdParams& p, int D, int dtype, hipStream_t stream) {
+int launch_bwd(const BwdParams& p, int D, int dtype, bool blockmask, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Hq * p.nq_pad;
   const dim3 block(kBwdThreads);
   const dim3 gpre((unsigned)((rows * 8 + kBwdThreads - 1) / kBwdThreads));
   const dim3 gkv((unsigned)((int64_t)p.B * p.Hkv * p.kv_slots));
   const dim3 gq((unsigned)((int64_t)p.B * p.Hq * p.q_slots));
   const bool f16in = dtype == ATTN_DTYPE_F16;
-  if (D == 64) {
-    if (f16in) launch_bwd_t<64, f16>(p, gpre, gkv, gq, block, stream);
-    else launch_bwd_t<64, bf16>(p, gpre, gkv, gq, block, stream);
+  if (blockmask) {
+    if (D == 64) {
+      if (f16in) launch_bwd_t<64, f16, true>(p, gpre, gkv, gq, block, stream);
+      else launch_bwd_t<64, bf16, true>(p, gpre, gkv, gq, block, stream);
+    } else {
+      if (f16in) launch_bwd_t<128, f16, true>(p, gpre, gkv, gq, block, stream);
+      else launch_bwd_t<128, bf16, true>(p, gpre, gkv, gq, block, stream);
+    }
+  } else if (D == 64) {
+    if (f16in) launch_bwd_t<64, f16, false>(p, gpre, gkv, gq, block, stream);
+    else launch_bwd_t<64, bf16, false>(p, gpre, gkv, gq, block, stream);
   } else {
-    if (f16in) launch_bwd_t<128, f16>(p, gpre, gkv, gq, block, stream);
-    else launch_bwd_t<128, bf16>(p, gpre, gkv, gq, block, stream);
+    if (f16in) launch_bwd_t<128, f16, false>(p, gpre, gkv, gq, block, stream);
+    else launch_bwd_t<128, bf16, false>(p, gpre, gkv, gq, block, stream);
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

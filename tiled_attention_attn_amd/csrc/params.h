@@ -32,6 +32,16 @@ struct FwdParams {
   uint32_t sched;  // ATTN_SCHED_* bits of the call
 };
 
+// BlockMask transposition: class map [Bm][Hm][nKt][nQt] from the lists.
+struct BmTransposeParams {
+  const int32_t* part_num;
+  const int32_t* part_idx;
+  const int32_t* full_num;
+  const int32_t* full_idx;
+  int Bm, Hm, nQt, nKt;
+  uint8_t* map_t;
+};
+
 // BlockMask builder.
 struct BmBuildParams {
   MaskParams mask;
@@ -94,6 +104,17 @@ struct BwdParams {
   float* ws_delta;  // [B*Hq][nq_pad]: rowsum(dO * O); 0 for padding
   int n_kt, kv_slots, kv_paired, kv_xcd_remap;  // 128-key tiles (dK / dV kernel)
   int n_qt, q_slots, q_paired, q_xcd_remap;     // 128-row tiles (dQ kernel)
+  // BlockMask (attn_bwd_blockmask): the forward lists [bm_B][bm_H][n_qt][n_kt]
+  // (dQ kernel) and the key-tile-major lists [bm_B][bm_H][n_kt][n_qt] (dK / dV).
+  const int32_t* part_num;
+  const int32_t* part_idx;
+  const int32_t* full_num;
+  const int32_t* full_idx;
+  const int32_t* tpart_num;
+  const int32_t* tpart_idx;
+  const int32_t* tfull_num;
+  const int32_t* tfull_idx;
+  int bm_B, bm_H;
   uint32_t sched;  // ATTN_SCHED_* bits of the call
 };
 
