@@ -433,6 +433,24 @@ def _sdwa(x, sel):
     raise ValueError(sel)
 
 
+def _mfma_layout(m):
+    """Index arrays of an MxMxK MFMA's operands (K = 8 * 64 / M).  A: lane l holds row
+    l % M, k = 8 (l / M) .. +7; B: column l % M, the same k.  D: for 32x32, register r of
+    lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32; for 16x16, row
+    4 (l / 16) + r, column l % 16."""
+    lanes = np.arange(LANES)
+    rows = np.repeat(lanes % m, 8)
+    ks = ((8 * (lanes // m))[:, None] + np.arange(8)).reshape(-1)
+    if m == 32:
+        drow = np.array([[8 * (r // 4) + 4 * (l // 32) + r % 4 for l in range(LANES)] for r in range(16)])
+    else:
+        drow = np.array([[4 * (l // 16) + r for l in range(LANES)] for r in range(4)])
+    return rows, ks, drow, lanes % m
+
+
+_MFMA_LAYOUT = {32: _mfma_layout(32), 16: _mfma_layout(16)}
+
+
 class Semantics:
     """One handler per opcode: ``op_<mnemonic>(wave, instr)``."""
 
@@ -1016,8 +1034,12 @@ class Semantics:
         for k, o in enumerate(i.args[1:4]):
             if ohi[k]:
                 raw = self.V(w, o)
-                x = ((raw >> 16) if osel[k] else (raw & 0xFFFF)).astype(np.uint16).view(np.float16).astype(np.float32)
-                x = -np.abs(x) if (o.abs and o.neg) else (np.abs(x) if o.abs else (-x if o.neg else x))
+                half = (raw >> 16) if osel[k] else (raw & 0xFFFF)
+                x = half.astype(np.uint16).view(np.float16).astype(np.float32)
+                if o.abs:
+                    x = np.abs(x)
+                if o.neg:
+                    x = -x
             else:
                 x = self.F(w, o)
             vals.append(x)
@@ -1109,20 +1131,7 @@ class Semantics:
     def op_v_accvgpr_read_b32(self, w, i): self.WV(w, i.args[0], self.V(w, i.args[1]))
     def op_v_accvgpr_mov_b32(self, w, i): self.WV(w, i.args[0], self.V(w, i.args[1]))
 
-    # ------------------------------------------------ MFMA
-    # A: lane l holds row l % M, k = 8 (l / M) .. +7; B: column l % M, the same k;
-    # D (32x32): register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32;
-    # D (16x16): register r of lane l is row 4 (l / 16) + r, column l % 16.
-    _L = np.arange(LANES)
-    _J = np.arange(8)
-    _IDX = {}
-    for _m in (32, 16):
-        _rows = np.repeat(_L % _m, 8)
-        _ks = ((8 * (_L // _m))[:, None] + _J).reshape(-1)
-        _IDX[_m] = (_rows, _ks)
-    _D32 = np.array([[8 * (r // 4) + 4 * (l // 32) + r % 4 for l in range(LANES)] for r in range(16)])
-    _D16 = np.array([[4 * (l // 16) + r for l in range(LANES)] for r in range(4)])
-
+    # ------------------------------------------------ MFMA (lane layouts: _MFMA_LAYOUT)
     def _halves(self, w, o, fp16):
         arr = w.v if o.kind == "v" else w.a
         w.check_read(o.kind, o.idx, 4)
@@ -1140,13 +1149,12 @@ class Semantics:
         nacc = 16 if m == 32 else 4
         k = 256 // m * 2  # 16 for 32x32, 32 for 16x16
         a, b = self._halves(w, A, fp16), self._halves(w, B, fp16)
-        rows, ks = self._IDX[m]
+        rows, ks, drow, dcol = _MFMA_LAYOUT[m]
         Am = np.zeros((m, k))
         Bm = np.zeros((k, m))
         Am[rows, ks] = a.reshape(-1)
         Bm[ks, rows] = b.reshape(-1)
-        Dm = Am @ Bm
-        out = Dm[self._D32, self._L % 32] if m == 32 else Dm[self._D16, self._L % 16]
+        out = (Am @ Bm)[drow, dcol]
         if C.kind in ("v", "a"):
             arr = w.v if C.kind == "v" else w.a
             w.check_read(C.kind, C.idx, nacc)
@@ -1193,7 +1201,10 @@ class Semantics:
         vals = np.zeros((max(nbytes // 4, 1), LANES), dtype=U32)
         for l in np.nonzero(lanes)[0]:
             raw = self.m.mem.read(int(addr[l]), nbytes)
-            vals[:, l] = raw.view(np.uint32) if nbytes >= 4 else int(raw.view(np.uint16)[0] if nbytes == 2 else raw[0])
+            if nbytes >= 4:
+                vals[:, l] = raw.view(np.uint32)
+            else:  # ushort / ubyte: zero-extended
+                vals[0, l] = int.from_bytes(raw.tobytes(), "little")
         self._queue_load(w, w.vm, dst, vals, lanes)
 
     def op_global_load_dword(self, w, i): self._gload(w, i, 4)
