@@ -1,5 +1,5 @@
-"""CPU replays of the compiled backward kernels (tests/isa_replay), and pins of the
-replay's own checks.
+"""CPU replays of compiled kernels (tests/isa_replay): the backward pass, the BlockMask
+backward and the paged decode; and pins of the replay's own checks.
 
 The dK/dV kernel's row searches once compiled to code that evaluated the "mask has
 documents" test as a lane mask inside a loop whose lanes leave one by one, and branched
@@ -7,7 +7,7 @@ on it in the next loop under another EXEC.  For the window-masked call below the
 lane sets were disjoint: the kernel took the document search and read through the null
 offsets pointer.  These tests replay the library's compiled kernels, with the launch
 arguments its host code computes, and require no out-of-bounds access, no lane-mask
-reuse and gradients within the GPU tests' bar of the fp64 oracle.
+reuse and results within the GPU tests' bars of the fp64 oracle.
 """
 import ctypes
 import math
@@ -22,6 +22,7 @@ import torch
 import oracle
 from oracle import backward as OBW, masks as M
 import workloads as W
+from gpu_util import assert_close
 
 HAVE_HIPCC = shutil.which("hipcc") is not None or os.path.exists("/opt/rocm/bin/hipcc")
 REL = 2.0 ** -7  # the gradient bar of the GPU backward tests: 2^-7 times the oracle's sum of |terms|
@@ -157,6 +158,41 @@ def test_blockmask_backward_per_head_maps_d128_replays_clean():
                                                row_block=256, bound=True, o_used=o.to(torch.float64).numpy())
     _check_grad(dk, rk, mk, "dK")
     _check_grad(dv, rv, mv, "dV")
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_paged_decode_with_empty_splits_replays_clean():
+    """Split-KV decode + combine over ragged sequences where most splits of the short ones
+    are empty (seq_lens 130, 1, 64 in 16-token pages, 9 splits): no fault, no race, no
+    lane-mask note, and O / LSE equal to the oracle's within the GPU tests' bars."""
+    from isa_replay.host import Replay
+    from oracle import paged as OP
+    rp = Replay(("decode",))
+    B, Hq, Hkv, Lq, Nk, D, ps, S = 3, 4, 2, 2, 130, 64, 16, 9
+    sl = [130, 1, 64]
+    wl = W.paged_decode("replay", B, Hq, Hkv, Lq, Nk, D, page_size=ps, pool_pages=B * 9 + 7, seed=3, seq_lens=sl)
+    t = wl.tensors
+    q, kp, vp, bt, lens = t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"]
+    ws_o = torch.full((B, Hq, Lq, S, D), float("nan"))
+    ws_l = torch.full((B, Hq, Lq, S), float("nan"))
+    o = torch.full((B, Hq, Lq, D), float("nan"), dtype=torch.bfloat16)
+    lse = torch.full((B, Hq, Lq), float("nan"))
+    rp.register(q=q, kp=kp, vp=vp, bt=bt, lens=lens, ws_o=ws_o, ws_l=ws_l, o=o, lse=lse)
+    st = rp.lib.attn_decode_splitkv(q.data_ptr(), _strides(q), kp.data_ptr(), vp.data_ptr(), kp.shape[0],
+                                    bt.data_ptr(), bt.stride(0), lens.data_ptr(), bt.shape[1], B, Hq, Hkv, Lq, D,
+                                    0, ps, S, wl.scale, None, None, ws_o.data_ptr(), ws_l.data_ptr(), None)
+    assert st == 0, st
+    st = rp.lib.attn_decode_combine(ws_o.data_ptr(), ws_l.data_ptr(), B, Hq, Lq, S, D, 0, o.data_ptr(),
+                                    _strides(o), lse.data_ptr(), None)
+    assert st == 0, st
+    rp.run()
+    assert [r[0].split("kernel")[0] for r in rp.ran] == ["_ZN5tattn13decode_", "_ZN5tattn14combine_"]
+    assert not rp.notes, rp.notes
+    for b in range(B):
+        kl = OP.gather(kp.to(torch.float64).numpy(), bt.numpy(), b, sl[b])[None]
+        vl = OP.gather(vp.to(torch.float64).numpy(), bt.numpy(), b, sl[b])[None]
+        ro, rl = oracle.attention(q[b:b + 1].to(torch.float64).numpy(), kl, vl, wl.scale, M.causal(Lq, sl[b]))
+        assert_close(o[b:b + 1].to(torch.float64).numpy(), lse[b:b + 1].numpy(), ro, rl, f"sequence {b}")
 
 
 # ---- pins of the replay's own checks, on hand-written assembly ----------------------
