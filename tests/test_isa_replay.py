@@ -195,6 +195,56 @@ def test_paged_decode_with_empty_splits_replays_clean():
         assert_close(o[b:b + 1].to(torch.float64).numpy(), lse[b:b + 1].numpy(), ro, rl, f"sequence {b}")
 
 
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_no_kernel_branches_on_a_lane_mask_from_a_lane_by_lane_loop():
+    """Every kernel of the library, statically: no compare made inside a loop whose lanes
+    leave one by one has its lane mask used with EXEC after that loop (the row-search
+    defect, which this check finds at 12 sites in the unfixed dK/dV kernels)."""
+    import glob
+    from isa_replay.host import Kernels, build
+    from isa_replay.static_checks import lane_mask_reuse_sites
+    from tiled_attention_attn_amd import build as B
+    names = tuple(os.path.basename(p)[:-4] for p in sorted(glob.glob(os.path.join(B.CSRC, "*.hip")))
+                  if not p.endswith("attn_api.hip"))
+    _, asm = build(names)
+    kernels = Kernels(list(asm.values()))
+    assert len(kernels.where) > 60
+    found = {n: lane_mask_reuse_sites(p, n) for n, p in kernels.where.items()}
+    assert not any(found.values()), {n: s for n, s in found.items() if s}
+
+
+_LOOP_ASM = """\
+probe:
+\ts_mov_b64 s[8:9], 0
+.LBB0_1:                                ; =>This Loop Header: Depth=1
+\tv_cmp_ne_u32_e64 s[6:7], 1, v1
+\tv_add_u32_e32 v2, 1, v2
+\tv_cmp_ge_u32_e32 vcc, v2, v0
+\ts_or_b64 s[8:9], vcc, s[8:9]
+\t{exit}
+\ts_cbranch_execnz .LBB0_1
+; %bb.2:
+\ts_or_b64 exec, exec, s[8:9]
+\ts_and_b64 vcc, exec, s[6:7]
+\ts_cbranch_vccnz .LBB0_3
+.LBB0_3:
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+def test_static_check_flags_only_lane_by_lane_loops():
+    from isa_replay.static_checks import lane_mask_reuse_sites
+    for exit_idiom, expected in (("s_andn2_b64 exec, exec, s[8:9]", 1), ("s_and_b64 s[10:11], exec, s[8:9]", 0)):
+        with tempfile.NamedTemporaryFile("w", suffix=".s", delete=False) as fh:
+            fh.write(_LOOP_ASM.format(exit=exit_idiom))
+        try:
+            sites = lane_mask_reuse_sites(fh.name, "probe")
+        finally:
+            os.unlink(fh.name)
+        assert len(sites) == expected, (exit_idiom, sites)
+
+
 # ---- pins of the replay's own checks, on hand-written assembly ----------------------
 _ASM = """\
 probe:
