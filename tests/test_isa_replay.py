@@ -1,5 +1,6 @@
-"""CPU replays of compiled kernels (tests/isa_replay): the backward pass, the BlockMask
-backward and the paged decode; and pins of the replay's own checks.
+"""CPU replays of compiled kernels (tests/isa_replay): the prefill kernels, the backward
+pass, the BlockMask backward and the paged decode; a static check of every kernel; and
+pins of the replay's and the check's own logic.
 
 The dK/dV kernel's row searches once compiled to code that evaluated the "mask has
 documents" test as a lane mask inside a loop whose lanes leave one by one, and branched
@@ -193,6 +194,68 @@ def test_paged_decode_with_empty_splits_replays_clean():
         vl = OP.gather(vp.to(torch.float64).numpy(), bt.numpy(), b, sl[b])[None]
         ro, rl = oracle.attention(q[b:b + 1].to(torch.float64).numpy(), kl, vl, wl.scale, M.causal(Lq, sl[b]))
         assert_close(o[b:b + 1].to(torch.float64).numpy(), lse[b:b + 1].numpy(), ro, rl, f"sequence {b}")
+
+
+_FWD_CASES = [
+    # (id, B, Hq, Hkv, N, D, mask flags, window, documents, per-head BlockMask maps)
+    ("causal_d64_gqa", 1, 4, 2, 700, 64, 1, None, None, False),            # fwd_kernel<64>
+    ("window_docs_d128_b2", 2, 2, 1, 600, 128, 2 | 4, (64, 64), [[100, 300, 200], [600]], False),  # ping-pong
+    ("blockmask_per_head_d128_b2", 2, 2, 1, 520, 128, 2, (100, 100), None, True),  # fwd_kernel<128, BlockMask>
+]
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+@pytest.mark.parametrize("case", _FWD_CASES, ids=[c[0] for c in _FWD_CASES])
+def test_forward_replays_clean(case):
+    """One replay per prefill kernel family: no fault, race or lane-mask note, and O / LSE
+    within the GPU tests' bars of the oracle."""
+    from isa_replay.host import Replay
+    from tiled_attention_attn_amd import _lib
+    name, B, Hq, Hkv, N, D, flags, window, docs, blockmask = case
+    rp = Replay(("fwd", "fwd_pp", "blockmask"))
+    g = W.generator(len(name))
+    q, k, v = (W.randn_bf16(g, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D)))
+    desc = _lib.attn_mask_desc(flags=flags, window_left=-1, window_right=-1)
+    mods = [M.causal(N, N)] if flags & 1 else []
+    if window is not None:
+        desc.window_left, desc.window_right = window
+        mods.append(M.window(window[0], window[1], N, N))
+    off = None
+    if docs is not None:
+        nd = max(len(d) for d in docs)
+        rows = [np.concatenate([[0], np.cumsum(d), np.full(nd - len(d), sum(d))]) for d in docs]
+        off = torch.tensor(np.stack(rows), dtype=torch.int32)
+        desc.doc_offsets, desc.num_docs, desc.doc_stride = off.data_ptr(), nd, off.stride(0)
+        mods.append(M.document(docs, N, N))
+    mod = M.and_(*mods)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, Hq, N), float("nan"))
+    rp.register(q=q, k=k, v=v, o=o, lse=lse, doc_offsets=off)
+    scale = 1.0 / math.sqrt(D)
+    if blockmask:
+        nt = (N + 127) // 128
+        tm = torch.stack([torch.stack([W.blockmask_tile_map(g, nt, 0.3) for _ in range(Hq)]) for _ in range(B)])
+        tm = tm.contiguous()
+        lists = [torch.zeros(B, Hq, nt, dtype=torch.int32), torch.zeros(B, Hq, nt, nt, dtype=torch.int32),
+                 torch.zeros(B, Hq, nt, dtype=torch.int32), torch.zeros(B, Hq, nt, nt, dtype=torch.int32)]
+        rp.register(tm=tm, **{f"lists{i}": t for i, t in enumerate(lists)})
+        bm = _lib.attn_blockmask(Bm=B, Hm=Hq, nQt=nt, nKt=nt, part_num=lists[0].data_ptr(),
+                                 part_idx=lists[1].data_ptr(), full_num=lists[2].data_ptr(),
+                                 full_idx=lists[3].data_ptr())
+        assert rp.lib.attn_build_blockmask(None, tm.data_ptr(), B, N, N, ctypes.byref(bm), None) == 0
+        st = rp.lib.attn_fwd_blockmask(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
+                                       _strides(v), o.data_ptr(), _strides(o), lse.data_ptr(), B, Hq, Hkv, N, N, D,
+                                       0, scale, ctypes.byref(desc), None, ctypes.byref(bm), None)
+        mod = M.blockmask(tm.numpy(), 128, mod)
+    else:
+        st = rp.lib.attn_fwd(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                             o.data_ptr(), _strides(o), lse.data_ptr(), B, Hq, Hkv, N, N, D, 0, scale,
+                             ctypes.byref(desc), None, None)
+    assert st == 0, st
+    rp.run()
+    assert not rp.notes, rp.notes
+    ro, rl = oracle.attention(*(x.to(torch.float64).numpy() for x in (q, k, v)), scale, mod)
+    assert_close(o.to(torch.float64).numpy(), lse.numpy(), ro, rl, name)
 
 
 @pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
