@@ -39,7 +39,7 @@ def _check_grad(got, ref, mag, what):
     assert not bad.any(), f"{what}: {int(bad.sum())} of {err.size} elements over the bar"
 
 
-def _backward_replay(B, Hq, Hkv, N, D, mask_flags, window=None, docs=None, kernels=None, seed=0):
+def _backward_replay(B, Hq, Hkv, N, D, mask_flags, window=None, docs=None, kernels=None, seed=0, schedule=0):
     """attn_bwd through the recorded host library, then a replay of its launches."""
     from isa_replay.host import Replay
     from tiled_attention_attn_amd import _lib
@@ -47,7 +47,9 @@ def _backward_replay(B, Hq, Hkv, N, D, mask_flags, window=None, docs=None, kerne
     g = W.generator(seed)
     q, k, v, do = (W.randn_bf16(g, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D), (B, Hq, N, D)))
     scale = 1.0 / math.sqrt(D)
-    mods, desc = [], _lib.attn_mask_desc(flags=mask_flags, window_left=-1, window_right=-1)
+    mods, desc = [], _lib.attn_mask_desc(flags=mask_flags | schedule, window_left=-1, window_right=-1)
+    if mask_flags & 1:
+        mods.append(M.causal(N, N))
     if window is not None:
         desc.window_left, desc.window_right = window
         mods.append(M.window(window[0], window[1], N, N))
@@ -101,6 +103,29 @@ def test_window_and_documents_backward_d128_replays_clean():
     assert not rp.notes, rp.notes
     _check_grad(dk, rk, mk, "dK")
     _check_grad(dv, rv, mv, "dV")
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_backward_schedules_replay_bitwise():
+    """The causal backward under the default schedule and under all three schedule flags
+    (no tile pairing, no XCD remap, work groups numbered in reverse).  Gradients start as
+    NaN, so a tile no work group covers would show; the two calls must agree bit for bit,
+    within the bar of the oracle.  With 8 heads of 256 rows both schedules launch a
+    multiple of 8 work groups, so the XCD remap is in play."""
+    from tiled_attention_attn_amd import _lib
+    runs = []
+    for sched in (0, _lib.SCHED_ALL):
+        rp, grads, ref = _backward_replay(1, 8, 8, 256, 64, 1, seed=14, schedule=sched)
+        assert not rp.notes, rp.notes
+        runs.append(([(r[0], r[1]) for r in rp.ran], grads, ref))
+    (ran0, g0, (rq, rk, rv, (mq, mk, mv))), (ran1, g1, _) = runs
+    assert [r[0] for r in ran0] == [r[0] for r in ran1]
+    assert ran0 != ran1, "the schedule flags left every grid unchanged"
+    for a, b, what in zip(g0, g1, ("dQ", "dK", "dV")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{what} differs between schedules"
+    _check_grad(g0[0], rq, mq, "dQ")
+    _check_grad(g0[1], rk, mk, "dK")
+    _check_grad(g0[2], rv, mv, "dV")
 
 
 @pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
