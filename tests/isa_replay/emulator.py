@@ -1438,9 +1438,19 @@ class Machine:
         self.lds_bytes, self.block, self.priv_bytes = max(lds_bytes, 4), block, priv_bytes
         self.notes, self._seen = [], set()
         self.steps = 0
+        self.executed = [0] * len(self.instrs)  # wave-level executions of each instruction
         sem = Semantics(self)
         self.handlers = [getattr(sem, "op_" + ins.op, None) for ins in self.instrs]
         self.missing = sorted({ins.op for ins, h in zip(self.instrs, self.handlers) if h is None})
+
+    def op_counts(self):
+        """Wave-level executions per mnemonic over the work groups run so far: what the
+        SQ_INSTS_* counters count per dispatch, for the groups replayed."""
+        out = {}
+        for ins, n in zip(self.instrs, self.executed):
+            if n:
+                out[ins.op] = out.get(ins.op, 0) + n
+        return out
 
     def note_once(self, key, msg):
         if key not in self._seen:
@@ -1462,10 +1472,12 @@ class Machine:
             if self.block - 64 * w.wid < 64:
                 w.exec = (1 << (self.block - 64 * w.wid)) - 1
         start = self.steps
+        executed = self.executed
         while True:
             for w in wg.waves:
                 while not w.done and not w.at_barrier:
                     ins = self.instrs[w.pc]
+                    executed[w.pc] += 1
                     w.pc += 1
                     try:
                         self.handlers[w.pc - 1](w, ins)

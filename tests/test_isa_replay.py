@@ -283,6 +283,90 @@ def test_forward_replays_clean(case):
     assert_close(o.to(torch.float64).numpy(), lse.numpy(), ro, rl, name)
 
 
+# SQ counters per dispatch, read with rocprofv3 --pmc on an MI355X for the causal
+# 2x16x4096x64 prefill (fwd_kernel<64>) and the paged decode (decode_kernel<128>); both
+# dispatches ran 2048 waves.  Values as profiles/sq_counters_causal_b2h16n4096d64_and_decode.md
+# lists them, to six or more significant digits.
+_SQ_COUNTERS = {
+    "prefill": dict(MFMA=2_162_688, VALU=19_935_200, TRANS=4_343_810, LDS=3_244_030),
+    "decode": dict(MFMA=8_388_608, VALU=141_860_000, TRANS=4_728_830, LDS=14_712_800),
+}
+_TRANS_OPS = ("v_exp_f32", "v_log_f32", "v_rcp_f32", "v_rcp_iflag_f32", "v_rsq_f32", "v_sqrt_f32", "v_sin_f32",
+              "v_cos_f32")
+
+
+def _classes(counts):
+    """Mnemonic counts -> the SQ_INSTS_* classes.  MFMAs issue as VALU instructions and are
+    counted in both; TRANS is the f32 transcendental subset of VALU."""
+    out = dict(MFMA=0, VALU=0, TRANS=0, LDS=0)
+    for op, n in counts.items():
+        if op.startswith("v_"):
+            out["VALU"] += n
+            out["MFMA"] += n * op.startswith("v_mfma")
+            out["TRANS"] += n * op.startswith(_TRANS_OPS)
+        out["LDS"] += n * op.startswith("ds_")
+    return out
+
+
+def _compare_with_counters(which, counts, waves):
+    hw = _SQ_COUNTERS[which]
+    got = _classes(counts)
+    for c in ("MFMA", "TRANS", "LDS"):
+        # equal, to the listed digits
+        assert abs(got[c] / waves - hw[c] / 2048) <= 0.05, f"{which} {c}: {got[c] / waves} vs {hw[c] / 2048} a wave"
+    # the prefill's VALU count is equal to the listed digits too; the decode's is 1.9 a wave
+    # (0.003%) above the listed count, a difference not traced to an instruction
+    assert abs(got["VALU"] / waves / (hw["VALU"] / 2048) - 1) <= 1e-4, f"{which} VALU: {got['VALU'] / waves}"
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_replay_instruction_counts_match_hardware_counters():
+    """The replay executes the instructions the GPU executed: per wave, its MFMA, VALU,
+    transcendental and LDS instruction counts over sampled work groups of the causal
+    2x16x4096x64 prefill (every work group runs 33 key steps) and of one (sequence, KV
+    head) row of the paged decode (all four splits; every row holds 32768 keys) agree with
+    the hardware counters of the full dispatches.  A wrong branch or loop trip in the replay
+    would move them.  The kernels are those the counters were read on; a kernel change
+    that moves these counts fails here until the counters are read again."""
+    from isa_replay.host import Replay
+    from tiled_attention_attn_amd import _lib
+    wl = W.causal_b2h16n4096d64()
+    q, k, v = (wl.tensors[x] for x in ("q", "k", "v"))
+    B, H, N, D = q.shape
+    rp = Replay(("fwd",))
+    o, lse = torch.zeros_like(q), torch.zeros(B, H, N)
+    rp.register(q=q, k=k, v=v, o=o, lse=lse)
+    desc = _lib.attn_mask_desc(flags=1, window_left=-1, window_right=-1)
+    assert rp.lib.attn_fwd(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                           o.data_ptr(), _strides(o), lse.data_ptr(), B, H, H, N, N, D, 0, wl.scale,
+                           ctypes.byref(desc), None, None) == 0
+    (L,) = rp.recorded()
+    assert L["grid"] == (512, 1, 1) and L["block"] == (256, 1, 1)
+    groups = [0, 333]
+    m = rp.run_launch(L, groups)
+    assert not m.notes, m.notes
+    _compare_with_counters("prefill", m.op_counts(), len(groups) * 4)
+
+    d = W.decode_b16h32kv8q16k32768d128()
+    t = d.tensors
+    q, kp, vp, bt, sl = t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"]
+    B, Hq, Lq, D = q.shape
+    Hkv = kp.shape[2]
+    rp = Replay(("decode",))
+    S = int(rp.lib.attn_decode_num_splits(B, Hkv, bt.shape[1], 256))
+    ws_o, ws_l = torch.zeros(B, Hq, Lq, S, D), torch.zeros(B, Hq, Lq, S)
+    rp.register(q=q, kp=kp, vp=vp, bt=bt, sl=sl, ws_o=ws_o, ws_l=ws_l)
+    assert rp.lib.attn_decode_splitkv(q.data_ptr(), _strides(q), kp.data_ptr(), vp.data_ptr(), kp.shape[0],
+                                      bt.data_ptr(), bt.stride(0), sl.data_ptr(), bt.shape[1], B, Hq, Hkv, Lq, D,
+                                      0, kp.shape[1], S, d.scale, None, None, ws_o.data_ptr(), ws_l.data_ptr(),
+                                      None) == 0
+    (L,) = rp.recorded()
+    assert L["grid"] == (S, Hkv, B) and L["block"] == (256, 1, 1)
+    m = rp.run_launch(L, list(range(S)))  # the splits of sequence 0, KV head 0
+    assert not m.notes, m.notes
+    _compare_with_counters("decode", m.op_counts(), S * 4)
+
+
 @pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
 def test_no_kernel_branches_on_a_lane_mask_from_a_lane_by_lane_loop():
     """Every kernel of the library, statically: no compare made inside a loop whose lanes
