@@ -291,26 +291,10 @@ _SQ_COUNTERS = {
     "prefill": dict(MFMA=2_162_688, VALU=19_935_200, TRANS=4_343_810, LDS=3_244_030),
     "decode": dict(MFMA=8_388_608, VALU=141_860_000, TRANS=4_728_830, LDS=14_712_800),
 }
-_TRANS_OPS = ("v_exp_f32", "v_log_f32", "v_rcp_f32", "v_rcp_iflag_f32", "v_rsq_f32", "v_sqrt_f32", "v_sin_f32",
-              "v_cos_f32")
-
-
-def _classes(counts):
-    """Mnemonic counts -> the SQ_INSTS_* classes.  MFMAs issue as VALU instructions and are
-    counted in both; TRANS is the f32 transcendental subset of VALU."""
-    out = dict(MFMA=0, VALU=0, TRANS=0, LDS=0)
-    for op, n in counts.items():
-        if op.startswith("v_"):
-            out["VALU"] += n
-            out["MFMA"] += n * op.startswith("v_mfma")
-            out["TRANS"] += n * op.startswith(_TRANS_OPS)
-        out["LDS"] += n * op.startswith("ds_")
-    return out
-
-
 def _compare_with_counters(which, counts, waves):
+    from isa_replay.mix import classes  # MFMAs count as VALU too; TRANS: the f32 transcendentals
     hw = _SQ_COUNTERS[which]
-    got = _classes(counts)
+    got = classes(counts)
     for c in ("MFMA", "TRANS", "LDS"):
         # equal, to the listed digits
         assert abs(got[c] / waves - hw[c] / 2048) <= 0.05, f"{which} {c}: {got[c] / waves} vs {hw[c] / 2048} a wave"
