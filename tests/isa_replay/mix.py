@@ -4,7 +4,8 @@ by the CPU replay of their compiled code.
 Every benchmark mask is the same for every head, so one head carries a dispatch's whole
 per-head work: the replay runs each call on head 0 of the workload's own tensors (for the
 GQA workload: KV head 0 and its four query heads), through the library's host code, and
-runs every work group of every launch.  Per-wave means are then those of the full
+runs every work group of every launch (the paged decode, whose rows all hold 32768 keys:
+the splits of one row).  Per-wave means are then those of the full
 dispatch, except for a few scalar instructions of the work-group numbering and for
 branches that depend on the data.  The backward calls take O and the LSE from the
 replayed forward call and the upstream gradient the benchmark draws.
@@ -14,9 +15,10 @@ The replay's instruction counts agree with the SQ counters of two dispatches
 count instructions, not cycles: they say how much VALU work a kernel issues per MFMA, not
 how well the two overlap.
 
-Usage, from tests/:  python -m isa_replay.mix [workload ...]   (all four by default: the
-forward calls of the prefill benchmarks, and the backward calls of the causal and the
-block-diffusion one; the block-diffusion backward takes the longest)
+Usage, from tests/:  python -m isa_replay.mix [workload ...]   (all five by default: the
+forward calls of the prefill benchmarks, the backward calls of the causal and the
+block-diffusion one, and the paged decode; the block-diffusion call and the BlockMask
+prefill take about an hour each)
 """
 from __future__ import annotations
 
@@ -80,18 +82,20 @@ class _Run:
         self.rp = Replay(sources)
         self.rows = []
 
-    def launches(self, label, heads_in_dispatch, skip=()):
-        """Runs every work group of the launches recorded since the last call."""
+    def launches(self, label, heads_in_dispatch, groups=None):
+        """Runs the launches recorded since the last call: every work group, or those
+        ``groups(launch)`` names (work groups that stand for the whole grid)."""
         for L in self.rp.recorded():
-            if any(s in L["name"] for s in skip):
-                continue
             t0 = time.time()
-            m = self.rp.run_launch(L)
+            ids = groups(L) if groups else None
+            m = self.rp.run_launch(L, ids)
             if m.notes:
                 raise RuntimeError(f"{L['name']}: {m.notes}")
             n_groups = L["grid"][0] * L["grid"][1] * L["grid"][2]
-            waves = n_groups * ((L["block"][0] + 63) // 64)
-            row = dict(label=label, kernel=L["name"], grid=L["grid"], waves=waves, scale=heads_in_dispatch,
+            per_group = (L["block"][0] + 63) // 64
+            waves = (len(ids) if ids is not None else n_groups) * per_group
+            row = dict(label=label, kernel=L["name"], grid=L["grid"], waves=waves,
+                       scale=heads_in_dispatch * n_groups * per_group / waves,
                        seconds=time.time() - t0, **classes(m.op_counts()))
             self.rows.append(row)
             print(format_row(row), flush=True)
@@ -117,7 +121,7 @@ def demangle(name):
     return out[5:] if out.startswith("void ") else out
 
 
-HEADER = ("| call | kernel | grid (one head) | waves | MFMA a wave | other VALU a wave | other VALU per MFMA "
+HEADER = ("| call | kernel | grid of the replayed call | waves replayed | MFMA a wave | other VALU a wave | other VALU per MFMA "
           "| f32 transcendental a wave | LDS a wave | global memory a wave | scalar ALU a wave "
           "| all instructions a wave | MFMA GFLOP, whole dispatch |\n"
           "|---|---|---|---|---|---|---|---|---|---|---|---|---|")
@@ -215,11 +219,37 @@ def blockmask_prefill(name="blockmask_gqa_b1h32kv8n32768d128"):
     return run.rows
 
 
+def paged_decode(name="decode_b16h32kv8q16k32768d128"):
+    """Split-KV + combine.  Every (sequence, KV head) row holds 32768 keys, so the splits of
+    row 0 stand for the split-KV grid; the combine runs whole."""
+    wl = W.decode_b16h32kv8q16k32768d128()
+    t = wl.tensors
+    q, kp, vp, bt, sl = t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"]
+    B, Hq, Lq, D = q.shape
+    Hkv = kp.shape[2]
+    run = _Run(("decode",))
+    S = int(run.rp.lib.attn_decode_num_splits(B, Hkv, bt.shape[1], 256))
+    ws_o, ws_l = torch.zeros(B, Hq, Lq, S, D), torch.zeros(B, Hq, Lq, S)
+    o, lse = torch.zeros(B, Hq, Lq, D, dtype=q.dtype), torch.zeros(B, Hq, Lq)
+    run.rp.register(q=q, kp=kp, vp=vp, bt=bt, sl=sl, ws_o=ws_o, ws_l=ws_l, o=o, lse=lse)
+    st = run.rp.lib.attn_decode_splitkv(q.data_ptr(), _s3(q), kp.data_ptr(), vp.data_ptr(), kp.shape[0],
+                                        bt.data_ptr(), bt.stride(0), sl.data_ptr(), bt.shape[1], B, Hq, Hkv, Lq,
+                                        D, 0, kp.shape[1], S, wl.scale, None, None, ws_o.data_ptr(),
+                                        ws_l.data_ptr(), None)
+    assert st == 0, st
+    st = run.rp.lib.attn_decode_combine(ws_o.data_ptr(), ws_l.data_ptr(), B, Hq, Lq, S, D, 0, o.data_ptr(),
+                                        _s3(o), lse.data_ptr(), None)
+    assert st == 0, st
+    run.launches(name, 1, groups=lambda L: list(range(S)) if "decode_kernel" in L["name"] else None)
+    return run.rows
+
+
 CALLS = {
     "causal_b2h16n4096d64": lambda: dense_prefill("causal_b2h16n4096d64", backward=True),
     "window_doc_b1h32n8192d128": lambda: dense_prefill("window_doc_b1h32n8192d128"),
     "blockdiff_b1h32n8192d128": lambda: dense_prefill("blockdiff_b1h32n8192d128", backward=True),
     "blockmask_gqa_b1h32kv8n32768d128": blockmask_prefill,
+    "decode_b16h32kv8q16k32768d128": paged_decode,
 }
 
 
