@@ -224,6 +224,51 @@ def _softcap_no_cap_factor(cap):
 _orig_softcap = OSM.softcap
 
 
+
+_orig_document = M.document
+_orig_key_range = M.key_range
+_orig_classify = OB.classify
+_orig_tile_lists = OB.tile_lists
+
+
+def _document_shifted(doc_lengths_per_batch, Nq, Nk):
+    """Document boundaries one token late (the first document one token longer)."""
+    lens = [[l[0] + 1, *l[1:-1], l[-1] - 1] if len(l) > 1 else list(l) for l in doc_lengths_per_batch]
+    return _orig_document(lens, Nq, Nk)
+
+
+def _key_range_inclusive(lo, hi):
+    def mod(b, h, q_idx, kv_idx):
+        k = np.asarray(kv_idx)
+        return np.broadcast_to((k >= lo) & (k <= hi), np.broadcast(np.asarray(q_idx), k).shape)
+    return mod
+
+
+def _classify_partial_as_full(mask_mod, b, h, Nq, Nk, tile):
+    c = _orig_classify(mask_mod, b, h, Nq, Nk, tile)
+    c[c == OB.PARTIAL] = OB.FULL
+    return c
+
+
+def _classify_padded_tiles(mask_mod, b, h, Nq, Nk, tile):
+    """Pairs past the sequence ends counted as hidden pairs of the tile."""
+    nqt, nkt = -(-Nq // tile), -(-Nk // tile)
+    out = np.zeros((nqt, nkt), dtype=np.uint8)
+    for i in range(nqt):
+        rows = np.arange(i * tile, (i + 1) * tile)
+        dm = np.zeros((tile, nkt * tile), dtype=bool)
+        dm[rows < Nq, :Nk] = M.dense(mask_mod, b, h, Nq, Nk, rows[rows < Nq])
+        for j in range(nkt):
+            blk = dm[:, j * tile:(j + 1) * tile]
+            out[i, j] = OB.EMPTY if not blk.any() else (OB.FULL if blk.all() else OB.PARTIAL)
+    return out
+
+
+def _tile_lists_classes_swapped(classes):
+    pn, pi, fn, fi = _orig_tile_lists(classes)
+    return fn, fi, pn, pi
+
+
 MUTANTS = {
     "scale_dropped": (OA, "scores", _scores_no_scale),
     "lse_without_max": (OA, "masked_softmax", _softmax_lse_no_max),
@@ -251,6 +296,11 @@ MUTANTS = {
     "softcap_jacobian_dropped": (OSM, "softcap", _softcap_no_jacobian),
     "softcap_jacobian_sign": (OSM, "softcap", _softcap_jacobian_sign),
     "softcap_cap_factor_dropped": (OSM, "softcap", _softcap_no_cap_factor),
+    "document_boundary_shifted": (M, "document", _document_shifted),
+    "key_range_inclusive_end": (M, "key_range", _key_range_inclusive),
+    "tile_class_partial_as_full": (OB, "classify", _classify_partial_as_full),
+    "tile_class_padded_tail": (OB, "classify", _classify_padded_tiles),
+    "tile_lists_classes_swapped": (OB, "tile_lists", _tile_lists_classes_swapped),
 }
 
 

@@ -367,6 +367,10 @@ def pin_blockmask_classes():
             d = [abs(a - b) for a in qs for b in ks]
             exp = 0 if min(d) > 3 else (2 if max(d) <= 3 else 1)
             assert cls2[i, j] == exp
+    # ragged causal, N=37: the last query tile holds 5 rows and the last key tile 5 keys;
+    # pairs past N do not count, so the last row's tiles left of the diagonal stay FULL
+    cls3 = OB.classify(M.causal(37, 37), 0, 0, 37, 37, 8)
+    assert np.array_equal(cls3, want)
     pn, pi, fn, fi = OB.tile_lists(want)
     assert list(pn) == [1] * 5 and list(fn) == [0, 1, 2, 3, 4]
     assert list(fi[4, :4]) == [0, 1, 2, 3] and list(pi[:, 0]) == [0, 1, 2, 3, 4]
