@@ -269,6 +269,36 @@ def _tile_lists_classes_swapped(classes):
     return fn, fi, pn, pi
 
 
+
+_orig_window = M.window
+_orig_and = M.and_
+_orig_smod_combine = OSM.combine
+
+
+def _window_top_left(left, right, Nq, Nk):
+    """Window positions not aligned to the end of the key sequence when Nq != Nk."""
+    return _orig_window(left, right, Nk, Nk)
+
+
+def _and_as_or(*mods):
+    def mod(b, h, q_idx, kv_idx):
+        out = None
+        for m in mods:
+            r = m(b, h, q_idx, kv_idx)
+            out = r if out is None else (out | r)
+        return out
+    return mod
+
+
+def _softmax_empty_rows_lse_zero(s, visible):
+    p, lse = _orig_softmax(s, visible)
+    return p, np.where(np.isfinite(lse), lse, 0.0)
+
+
+def _smod_combine_reversed(*mods):
+    """The score changes applied in reverse order (the soft-cap after the additive terms)."""
+    return _orig_smod_combine(*reversed(mods))
+
 MUTANTS = {
     "scale_dropped": (OA, "scores", _scores_no_scale),
     "lse_without_max": (OA, "masked_softmax", _softmax_lse_no_max),
@@ -301,6 +331,10 @@ MUTANTS = {
     "tile_class_partial_as_full": (OB, "classify", _classify_partial_as_full),
     "tile_class_padded_tail": (OB, "classify", _classify_padded_tiles),
     "tile_lists_classes_swapped": (OB, "tile_lists", _tile_lists_classes_swapped),
+    "window_top_left": (M, "window", _window_top_left),
+    "mask_and_as_or": (M, "and_", _and_as_or),
+    "empty_row_lse_zero": (OA, "masked_softmax", _softmax_empty_rows_lse_zero),
+    "score_mod_order_reversed": (OSM, "combine", _smod_combine_reversed),
 }
 
 

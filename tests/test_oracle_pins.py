@@ -68,6 +68,7 @@ BRUTE_CASES = [
     ("window_sym", 1, 1, 1, 13, 13, 4, {"window": (2, 2)}),
     ("window_asym_causal", 1, 1, 1, 12, 12, 3, {"window": (3, 1), "causal": True}),
     ("window_left_unbounded", 1, 1, 1, 10, 10, 3, {"window": (-1, 1)}),
+    ("window_bottom_right", 1, 1, 1, 5, 12, 3, {"window": (2, 1)}),
     ("documents", 1, 2, 2, 14, 14, 4, {"docs": [3, 6, 5]}),
     ("window_and_documents", 1, 1, 1, 16, 16, 4, {"window": (2, 2), "docs": [5, 4, 7]}),
     ("block_diffusion", 1, 1, 1, 13, 13, 4, {"block": 4}),
