@@ -10,14 +10,16 @@ A mask spec is a dict with any of:
     window: (left, right)      keys p-left .. p+right (negative = unbounded)
     docs: [len, ...]           keys of the document holding p
     block: bs                  keys 0 .. (p // bs + 1) * bs - 1
-    tiles: (tile_map, T, inner_spec)   BlockMask over raw query index q
+    tiles: (tile_map, T, inner_spec)   BlockMask over raw query index q; tile_map is
+                               [q tile][k tile], or [Bm][Hm][q tile][k tile] with a
+                               size-1 batch or head level shared
     key_range: (lo, hi)        keys lo .. hi - 1
 with p = q + (Nk - Nq).
 """
 import math
 
 
-def _range_keys(spec, q, Nq, Nk):
+def _range_keys(spec, q, Nq, Nk, b=0, h=0):
     p = q + (Nk - Nq)
     keys = set(range(Nk))
     if spec.get("causal"):
@@ -43,7 +45,10 @@ def _range_keys(spec, q, Nq, Nk):
         keys &= set(range(lo, hi))
     if "tiles" in spec:
         tmap, T, inner = spec["tiles"]
-        inner_keys = set(_range_keys(inner, q, Nq, Nk))
+        if isinstance(tmap[0][0], (list, tuple)):  # one map per (batch, head)
+            tmap = tmap[b if len(tmap) > 1 else 0]
+            tmap = tmap[h if len(tmap) > 1 else 0]
+        inner_keys = set(_range_keys(inner, q, Nq, Nk, b, h))
         allowed = set()
         for kt in range(len(tmap[0])):
             state = int(tmap[q // T][kt])
@@ -102,7 +107,7 @@ def attention(q, k, v, scale, spec, score_spec=None):
             kv = h // G
             Oh, Lh = [], []
             for i in range(Nq):
-                keys = _range_keys(spec, i, Nq, Nk)
+                keys = _range_keys(spec, i, Nq, Nk, b, h)
                 dv = len(v[b][kv][0]) if Nk else len(q[b][h][i])
                 if not keys:
                     Oh.append([0.0] * dv)

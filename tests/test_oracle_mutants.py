@@ -299,6 +299,16 @@ def _smod_combine_reversed(*mods):
     """The score changes applied in reverse order (the soft-cap after the additive terms)."""
     return _orig_smod_combine(*reversed(mods))
 
+
+_orig_blockmask = M.blockmask
+
+
+def _blockmask_first_map_only(tile_map, tile, partial_mod):
+    """Per-(batch, head) tile maps read as the map of batch 0, head 0."""
+    tm = np.asarray(tile_map)
+    return _orig_blockmask(tm if tm.ndim == 2 else tm[0, 0], tile, partial_mod)
+
+
 MUTANTS = {
     "scale_dropped": (OA, "scores", _scores_no_scale),
     "lse_without_max": (OA, "masked_softmax", _softmax_lse_no_max),
@@ -335,6 +345,7 @@ MUTANTS = {
     "mask_and_as_or": (M, "and_", _and_as_or),
     "empty_row_lse_zero": (OA, "masked_softmax", _softmax_empty_rows_lse_zero),
     "score_mod_order_reversed": (OSM, "combine", _smod_combine_reversed),
+    "blockmask_first_map_only": (M, "blockmask", _blockmask_first_map_only),
 }
 
 

@@ -79,6 +79,9 @@ BRUTE_CASES = [
     ("blockmask_ragged", 1, 1, 1, 10, 10, 3,
      {"tiles": ([[1, 0, 0], [0, 1, 0], [2, 0, 1]], 4, {"causal": True})}),
     ("empty_rows", 1, 1, 1, 6, 6, 3, {"docs": [6], "key_range": (4, 6), "causal": True}),
+    ("blockmask_per_batch_and_head", 2, 2, 1, 8, 8, 3,
+     {"tiles": ([[[[1, 0], [2, 1]], [[1, 2], [0, 0]]], [[[0, 0], [0, 1]], [[2, 2], [2, 2]]]], 4,
+                {"window": (1, 1)})}),
 ]
 
 
