@@ -124,7 +124,8 @@ def test_fwd_blockmask_from_predicate_matches_dense():
 
 def test_config4_blockmask_gqa_b1h32kv8n32768d128_every_head_sampled_rows():
     """Block-sparse GQA prefill at full size: builder bitwise vs the map, every head on sampled
-    rows (first and last 8, 32 random) vs the oracle."""
+    rows (first and last 8, 32 random) vs the oracle, and every row of the first and the last
+    head (KV heads 0 and 7)."""
     announce("blockmask_gqa_b1h32kv8n32768d128")
     wl = W.blockmask_gqa_b1h32kv8n32768d128()
     tm = wl.mask["tile_map"]
@@ -146,3 +147,8 @@ def test_config4_blockmask_gqa_b1h32kv8n32768d128_every_head_sampled_rows():
         rows = sample_rows(N, 32, h)
         ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, 0, h, rows)
         assert_close(f64(o[0, h, rows]), f64(lse[0, h, rows]), ro, rl, f"cfg4 h{h}")
+    for h in (0, 31):
+        for r0 in range(0, N, 2048):
+            rows = np.arange(r0, r0 + 2048)
+            ro, rl = oracle.attention_rows(qa, ka, va, wl.scale, mod, 0, h, rows)
+            assert_close(f64(o[0, h, rows]), f64(lse[0, h, rows]), ro, rl, f"cfg4 h{h} rows {r0}+2048")
