@@ -400,3 +400,56 @@ def test_binding_rejects_bad_tensors_before_any_call(T):
         T.attn_decode_combine(ws_o, ws_l, torch.zeros(3, 4, 2, 128, **bf))
     with pytest.raises(ValueError, match="shape"):
         T.attn_decode_combine(ws_o, torch.zeros(3, 4, 2, 3), torch.zeros(3, 4, 2, 64, **bf))
+
+
+def test_header_compiles_as_c_and_matches_the_binding(T, tmp_path):
+    """tests/abi_from_c.c, plain C11 built with gcc -Wall -Wextra -Werror against the
+    header and linked against the library, reports the header's struct layouts,
+    constants and a few host-only results; each must equal what the ctypes binding
+    uses, so a field or constant changed on one side only fails here."""
+    import json
+    import shutil
+    import subprocess
+    from tiled_attention_attn_amd import _lib as L
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("needs gcc")
+    pkg = os.path.dirname(T.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "abi_from_c.c"), "-L", pkg, "-ltiled_attn",
+           f"-Wl,-rpath,{pkg}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = json.loads(subprocess.run([exe], capture_output=True, text=True, check=True).stdout)
+
+    for cname, cls in (("attn_mask_desc", L.attn_mask_desc), ("attn_score_mod", L.attn_score_mod),
+                       ("attn_blockmask", L.attn_blockmask), ("attn_auto_plan", L.attn_auto_plan)):
+        assert out[f"sizeof {cname}"] == ctypes.sizeof(cls), cname
+        c_fields = {k.split(".", 1)[1] for k in out if k.startswith(cname + ".")}
+        assert c_fields == {f for f, _ in cls._fields_}, cname
+        for f, _ in cls._fields_:
+            fld = getattr(cls, f)
+            assert out[f"{cname}.{f}"] == [fld.offset, fld.size], f"{cname}.{f}"
+
+    for c, py in (("ATTN_DTYPE_BF16", T.DTYPE_BF16), ("ATTN_DTYPE_F16", T.DTYPE_F16),
+                  ("ATTN_MASK_CAUSAL", L.MASK_CAUSAL), ("ATTN_MASK_WINDOW", L.MASK_WINDOW),
+                  ("ATTN_MASK_DOCUMENT", L.MASK_DOCUMENT), ("ATTN_MASK_BLOCK_CAUSAL", L.MASK_BLOCK_CAUSAL),
+                  ("ATTN_SCHED_NO_PAIRING", L.SCHED_NO_PAIRING), ("ATTN_SCHED_NO_XCD_REMAP", L.SCHED_NO_XCD_REMAP),
+                  ("ATTN_SCHED_REVERSE", L.SCHED_REVERSE), ("ATTN_SCORE_ALIBI", L.SCORE_ALIBI),
+                  ("ATTN_SCORE_ALIBI_SYM", L.SCORE_ALIBI_SYM), ("ATTN_SCORE_REL_BIAS", L.SCORE_REL_BIAS),
+                  ("ATTN_SCORE_SOFTCAP", L.SCORE_SOFTCAP), ("ATTN_BLOCKMASK_TILE", L.BLOCKMASK_TILE),
+                  ("ATTN_PATH_PREFILL", L.PATH_PREFILL), ("ATTN_PATH_SPLITKV", L.PATH_SPLITKV)):
+        assert out[c] == py, c
+
+    lib = T.lib_handle()
+    assert out["fwd_null"] == out["ATTN_ERR_NULL"]
+    plan = L.attn_auto_plan()
+    assert lib.attn_fwd_auto_plan(16, 32, 8, 16, 32768, 128, None, ctypes.byref(plan)) == 0
+    assert out["plan"] == [0, plan.path, plan.num_splits, plan.workspace_bytes]
+    assert out["plan"][1] == out["ATTN_PATH_SPLITKV"]
+    assert out["bwd_ws"] == T.attn_bwd_workspace_bytes(2, 16, 4096)
+    assert out["bm_bytes"] == T.attn_blockmask_bytes(1, 1, 256, 256)
+    assert out["noalloc_max"] == T.attn_decode_noalloc_max_bytes()
+    assert out["status_head_dim"] == T.attn_status_str(out["ATTN_ERR_HEAD_DIM"])
