@@ -176,6 +176,46 @@ def test_blockmask_and_decode_argument_errors(T):
     assert lib.attn_decode_ws_o_bytes(16, 32, 16, 128, 4) == 16 * 32 * 16 * 4 * 128 * 4
 
 
+
+def test_extreme_sizes_are_rejected_without_overflow(T):
+    """Sizes whose products pass 32 or 64 bits: the checks compute them without overflow
+    (cases found by the UBSan run of tests/test_host_ub.py) and refuse them before any
+    launch, or the size helpers answer 0 ("invalid sizes")."""
+    lib = T.lib_handle()
+    IMAX = 2**31 - 1
+    qs = _strides(32 * 16 * 128, 16 * 128, 128)
+    # num_docs + 1 and 2 * rel_radius + 1 at INT_MAX
+    md = T.attn_mask_desc(flags=T.MASK_DOCUMENT, doc_offsets=16, num_docs=IMAX, doc_stride=IMAX)
+    assert lib.attn_fwd(16, qs, 32, qs, 48, qs, 64, qs, None, 1, 4, 4, 16, 16, 128, 0, 0.1,
+                        ctypes.byref(md), None, None) == -7
+    sm = T.attn_score_mod(flags=T.SCORE_REL_BIAS, rel_bias=16, rel_radius=IMAX)
+    assert lib.attn_fwd(16, qs, 32, qs, 48, qs, 64, qs, None, 1, 4, 4, 16, 16, 128, 0, 0.1, None,
+                        ctypes.byref(sm), None) == -13
+    # size helpers: products beyond 2^64 give 0
+    assert lib.attn_decode_ws_o_bytes(IMAX, IMAX, IMAX, 128, 65536) == 0
+    assert lib.attn_decode_ws_lse_bytes(IMAX, IMAX, IMAX, IMAX) == 0
+    assert lib.attn_bwd_workspace_bytes(IMAX, IMAX, IMAX) == 0
+    assert lib.attn_blockmask_bytes(65535, 65535, 2**21, 2**21) == 0
+    assert lib.attn_blockmask_bytes(1, 1, 256, 256) == 256 * 8 + 256 * 256 * 8
+    assert lib.attn_decode_num_splits(1, 1, IMAX, 256) == -(-IMAX // 2048)
+    # split-KV partials of more bytes than a size_t holds: no workspace can exist
+    assert lib.attn_decode_splitkv(16, qs, 32, 48, 10, 64, 65536, 80, 65536, 65535, 65535, 65535, 65536,
+                                   128, 0, 16, 65536, 0.1, None, None, 96, 112, None) == -2
+    # combine: B * Hq * Lq past 2^31 - 4 rows (the product itself past 2^63 too)
+    assert lib.attn_decode_combine(16, 16, IMAX, IMAX, IMAX, 1, 64, 0, 32, qs, None, None) == -2
+    assert lib.attn_decode_combine(16, 16, 1, 1, IMAX - 2, 1, 64, 0, 32, qs, None, None) == -2
+    # transposition of a map with more than 2^64 entries
+    bm = T.attn_blockmask(Bm=65535, Hm=65535, nQt=2**21, nKt=2**21, part_num=16, part_idx=32,
+                          full_num=48, full_idx=64)
+    bt = T.attn_blockmask(Bm=65535, Hm=65535, nQt=2**21, nKt=2**21, part_num=16, part_idx=32,
+                          full_num=48, full_idx=64)
+    assert lib.attn_blockmask_transpose(ctypes.byref(bm), ctypes.byref(bt), 16, 2**63, None) == -10
+    # a decode-shaped auto call whose combine would number more than 2^31 - 4 rows stays on
+    # the prefill path; one just below the bound takes split-KV
+    P = T.attn_fwd_auto_plan
+    assert P(65535, 65535, 65535, 1, 512, 64).path == T.PATH_PREFILL
+    assert P(32767, 65535, 65535, 1, 512, 64).path == T.PATH_SPLITKV
+
 def test_bwd_argument_errors(T):
     lib = T.lib_handle()
     qs = _strides(64 * 256, 64 * 256, 64)

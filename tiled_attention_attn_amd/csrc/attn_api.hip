@@ -4,6 +4,7 @@
 // freed or synchronised here (see include/tiled_attn.h for the contract).
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "params.h"
 
@@ -26,6 +27,15 @@ constexpr int kMaxLen = 1 << 28;  // keeps every key / row index and product in 
 constexpr int64_t kMaxRowStride = (int64_t)1 << 24;  // sequence stride of streamed tiles
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Product of byte-count factors, or 0 when it does not fit a size_t (the size
+// helpers' "invalid sizes" answer).
+size_t checked_product(std::initializer_list<size_t> factors) {
+  size_t r = 1;
+  for (size_t f : factors)
+    if (__builtin_mul_overflow(r, f, &r)) return 0;
+  return r;
+}
 
 int check_strides(const int64_t s[3]) {
   if (s == nullptr) return ATTN_ERR_NULL;
@@ -61,7 +71,7 @@ int make_mask(const attn_mask_desc* m, int Nq, int Nk, bool allow_doc, MaskParam
   if (m->flags & ATTN_MASK_DOCUMENT) {
     if (!allow_doc) return ATTN_ERR_MASK;
     if (m->doc_offsets == nullptr) return ATTN_ERR_NULL;
-    if (m->num_docs < 1 || m->doc_stride < m->num_docs + 1) return ATTN_ERR_MASK;
+    if (m->num_docs < 1 || (int64_t)m->doc_stride < (int64_t)m->num_docs + 1) return ATTN_ERR_MASK;
     if (Nq > Nk) return ATTN_ERR_MASK;
     out.doc = m->doc_offsets;
     out.num_docs = m->num_docs;
@@ -81,7 +91,7 @@ int make_smod(const attn_score_mod* m, float scale, int G_bwd, ScoreParams& out)
   if ((f & (ATTN_SCORE_ALIBI | ATTN_SCORE_ALIBI_SYM)) && m->slopes == nullptr) return ATTN_ERR_NULL;
   if (f & ATTN_SCORE_REL_BIAS) {
     if (m->rel_bias == nullptr) return ATTN_ERR_NULL;
-    if (m->rel_radius < 0 || 2 * m->rel_radius + 1 > kMaxRelTable) return ATTN_ERR_SCORE_MOD;
+    if (m->rel_radius < 0 || m->rel_radius > (kMaxRelTable - 1) / 2) return ATTN_ERR_SCORE_MOD;
     if (G_bwd > 0 && (int64_t)G_bwd * (2 * m->rel_radius + 1) > 8192) return ATTN_ERR_SCORE_MOD;
   }
   if (f & ATTN_SCORE_SOFTCAP) {
@@ -174,6 +184,8 @@ AutoPlan auto_plan(int B, int Hq, int Hkv, int Nq, int Nk, int D, const attn_sco
   AutoPlan pl{ATTN_PATH_PREFILL, 0, 0, 0, 0};
   const long rows = (long)(Hq / Hkv) * Nq;
   if (Nq < 1 || rows > 64 || Nk < kAutoMinKeys) return pl;
+  // the combine numbers its B * Hq * Nq rows in int (as attn_decode_combine bounds them)
+  if ((long)B * Hq * Nq > 0x7fffffffL - 3) return pl;
   const long units = (long)B * Hkv;
   long S = units > 0 ? (kAutoTargetGroups + units - 1) / units : 1;
   const long max_s = Nk / kAutoSplitKeys;
@@ -343,8 +355,13 @@ int attn_fwd(const void* q, const int64_t q_stride[3], const void* k, const int6
 
 size_t attn_blockmask_bytes(int Bm, int Hm, int nQt, int nKt) {
   if (Bm <= 0 || Hm <= 0 || nQt < 0 || nKt < 0) return 0;
-  const size_t rows = (size_t)Bm * Hm * nQt;
-  return rows * 4 * 2 + rows * (size_t)nKt * 4 * 2;
+  const size_t counts = checked_product({(size_t)Bm, (size_t)Hm, (size_t)nQt, 2 * sizeof(int32_t)});
+  const size_t lists = checked_product({counts, (size_t)nKt});
+  size_t total = 0;
+  if ((nQt > 0 && counts == 0) || (nKt > 0 && counts != 0 && lists == 0) ||
+      __builtin_add_overflow(counts, lists, &total))
+    return 0;
+  return total;
 }
 
 int attn_build_blockmask(const attn_mask_desc* mask, const uint8_t* tile_map, int B, int Nq,
@@ -399,12 +416,13 @@ int attn_fwd_blockmask(const void* q, const int64_t q_stride[3], const void* k,
 
 size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits) {
   if (B < 0 || Hq < 0 || Lq < 0 || D <= 0 || num_splits <= 0) return 0;
-  return (size_t)B * Hq * Lq * num_splits * D * sizeof(float);
+  return checked_product({(size_t)B, (size_t)Hq, (size_t)Lq, (size_t)num_splits, (size_t)D,
+                          sizeof(float)});
 }
 
 size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits) {
   if (B < 0 || Hq < 0 || Lq < 0 || num_splits <= 0) return 0;
-  return (size_t)B * Hq * Lq * num_splits * sizeof(float);
+  return checked_product({(size_t)B, (size_t)Hq, (size_t)Lq, (size_t)num_splits, sizeof(float)});
 }
 
 int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
@@ -417,7 +435,7 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus) {
   const long target = 2L * num_cus;
   long s = (target + units - 1) / units;
   if (s < 1) s = 1;
-  const long min_s = (max_pages + 2047) / 2048;
+  const long min_s = ((long)max_pages + 2047) / 2048;
   if (s < min_s) s = min_s;
   if (s > max_pages) s = max_pages;
   return (int)s;
@@ -472,6 +490,8 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3], const void* k_
   p.rows = G * Lq;
   p.n_rg = (p.rows + 63) / 64;
   if ((long)p.S * p.n_rg > 0x7fffffffL) return ATTN_ERR_SHAPE;
+  // partials of more bytes than a size_t holds: no workspace can be that large
+  if (attn_decode_ws_o_bytes(B, Hq, Lq, D, num_splits) == 0) return ATTN_ERR_SHAPE;
   p.c2 = scale * 1.4426950408889634f;
   p.ws_o = ws_o;
   p.ws_lse = ws_lse;
@@ -485,7 +505,11 @@ int attn_decode_combine(const float* ws_o, const float* ws_lse, int B, int Hq, i
   int st = check_strides(o_stride);
   if (st) return st;
   if (B < 0 || Hq < 0 || Lq < 0) return ATTN_ERR_SHAPE;
-  if ((long)B * Hq * Lq > 0x7fffffffL) return ATTN_ERR_SHAPE;
+  // B * Hq < 2^62; the product with Lq may not fit.  The combine kernel numbers
+  // rows 4 * group + wave in int, so its last group must stay below 2^31.
+  int64_t rows = 0;
+  if (__builtin_mul_overflow((int64_t)B * Hq, (int64_t)Lq, &rows) || rows > 0x7fffffffL - 3)
+    return ATTN_ERR_SHAPE;
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if ((st = check_dtype(dtype))) return st;
   if (S < 1 || S > 65536) return ATTN_ERR_WORKSPACE;
@@ -557,7 +581,7 @@ int attn_fwd_auto(const void* q, const int64_t q_stride[3], const void* k,
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
   if (B < 0 || Hq < 0 || Nq < 0) return 0;
   const size_t pad = ((size_t)Nq + 63) / 64 * 64;
-  return 2 * (size_t)B * Hq * pad * sizeof(float);
+  return checked_product({2, (size_t)B, (size_t)Hq, pad, sizeof(float)});
 }
 
 int attn_bwd(const void* q, const int64_t q_stride[3], const void* k, const int64_t k_stride[3],
@@ -600,8 +624,10 @@ int attn_blockmask_transpose(const attn_blockmask* bm, attn_blockmask* out, uint
     return ATTN_ERR_BLOCKMASK;
   if (out->Bm != bm->Bm || out->Hm != bm->Hm || out->nQt != bm->nKt || out->nKt != bm->nQt)
     return ATTN_ERR_BLOCKMASK;
-  const size_t need = (size_t)bm->Bm * bm->Hm * bm->nQt * bm->nKt;
-  if (need == 0) return ATTN_OK;
+  if (bm->nQt == 0 || bm->nKt == 0) return ATTN_OK;
+  const size_t need = checked_product({(size_t)bm->Bm, (size_t)bm->Hm, (size_t)bm->nQt,
+                                       (size_t)bm->nKt});
+  if (need == 0) return ATTN_ERR_BLOCKMASK;  // more map bytes than a size_t holds
   if (map_tmp == nullptr) return ATTN_ERR_NULL;
   if (map_tmp_bytes < need) return ATTN_ERR_WORKSPACE;
   BmTransposeParams tp{bm->part_num, bm->part_idx, bm->full_num, bm->full_idx,

@@ -405,7 +405,7 @@ int launch_combine(const float* ws_o, const float* ws_lse, int B, int Hq, int Lq
                    int dtype, void* o, int64_t o_sb, int64_t o_sh, int64_t o_sn, float* lse,
                    hipStream_t stream) {
   const int n_rows = B * Hq * Lq;
-  dim3 grid((n_rows + 3) / 4), block(256);
+  dim3 grid((unsigned)(((int64_t)n_rows + 3) / 4)), block(256);
   if (dtype == ATTN_DTYPE_F16)
     launch_combine_t<f16>(ws_o, ws_lse, n_rows, Hq, Lq, S, D, o, o_sb, o_sh, o_sn, lse, grid, block, stream);
   else
