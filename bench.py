@@ -484,6 +484,18 @@ def cpu_oracle_samples():
     return out
 
 
+def _leg(result, key, fn):
+    """Runs one secondary leg.  A Python-level failure there (an argument error, a shape
+    mistake) is recorded under result[key] = {"error": ...} instead of losing the
+    headline line; it is logged and returns None."""
+    try:
+        return fn()
+    except Exception as e:  # noqa: BLE001 - reported in the JSON line, not swallowed
+        log(f"{key} failed: {type(e).__name__}: {e}")
+        result[key] = {"error": f"{type(e).__name__}: {e}"}
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,8 +576,10 @@ def main():
                      "executed_gflop": round(pf["executed_flops"] / 1e9, 3),
                      "executed_tflops": round(pf["executed_flops"] / pf["avg_ms"] / 1e9, 2)},
     }
+    dec = others = bwd = None
     if not args.quick and args.only == "all":
-        dec = bench_decode(T, W, args.steps, args.warmup)
+        dec = _leg(result, "decode", lambda: bench_decode(T, W, args.steps, args.warmup))
+    if dec is not None:
         kvb = dec["kv_bytes"]
         step_ms, split_ms = dec["step"]["median_ms"], dec["split"]["median_ms"]
         gbs = kvb / step_ms / 1e6
@@ -573,8 +587,10 @@ def main():
         log(f"decode: {step_ms*1e3:.1f} us median (splitkv {split_ms*1e3:.1f} + combine "
             f"{dec['comb']['median_ms']*1e3:.1f}), {gbs:.0f} GB/s, S={dec['splits']}; "
             f"{dec['avg_ms']*1e3:.1f} us mean over {args.steps} back-to-back steps")
-        st = bench_stream(T)
-        log(f"stream read ceiling: {st['median_gbs']:.0f} GB/s median, {st['best_gbs']:.0f} best")
+        err = {}
+        st = _leg(err, "read_ceiling", lambda: bench_stream(T))
+        if st is not None:
+            log(f"stream read ceiling: {st['median_gbs']:.0f} GB/s median, {st['best_gbs']:.0f} best")
         result["decode"] = {
             "workload": "decode_b16h32kv8q16k32768d128", "value": round(gbs, 1), "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -593,11 +609,12 @@ def main():
                          "traffic_unit": "bytes/launch",
                          "kernel": "decode_kernel<128, bf16, false, true>",
                          "kernel_median_us": round(split_ms * 1e3, 2)},
-            "read_ceiling": {"what": "attn_probe_stream_read: plain streaming read of 2 GiB, one "
-                                     "256-thread group per CU, median of the same series",
-                             "median_gbs": round(st["median_gbs"], 1),
-                             "best_gbs": round(st["best_gbs"], 1),
-                             "decode_frac_of_ceiling": round(gbs / st["median_gbs"], 4)},
+            "read_ceiling": err.get("read_ceiling") if st is None else {
+                "what": "attn_probe_stream_read: plain streaming read of 2 GiB, one "
+                        "256-thread group per CU, median of the same series",
+                "median_gbs": round(st["median_gbs"], 1),
+                "best_gbs": round(st["best_gbs"], 1),
+                "decode_frac_of_ceiling": round(gbs / st["median_gbs"], 4)},
             "auto_contiguous": {
                 "what": "attn_fwd_auto on the same keys in contiguous [B, Hkv, Nk, D] K/V "
                         "(split-KV + combine, chosen by shape) vs attn_fwd (prefill kernels)",
@@ -609,14 +626,17 @@ def main():
                 "speedup": round(dec["auto_prefill"]["median_ms"] / dec["auto"]["median_ms"], 2)},
         }
     if not args.quick:
-        others = bench_prefill_others(T, W, args.steps, args.warmup)
+        others = _leg(result, "prefill_other", lambda: bench_prefill_others(T, W, args.steps, args.warmup))
+    if not args.quick and others is not None:
         for o in others:
             log(f"prefill {o['workload']}: {o['avg_ms']*1e3:.1f} us, {o['tflops']:.1f} TFLOP/s "
                 f"(median {o['median_ms']*1e3:.1f} us; executed {o['executed_gflop']:.1f} of "
                 f"useful {o['useful_gflop']:.1f} GFLOP)")
         result["prefill_other"] = [{k: (round(v, 4) if isinstance(v, float) else v)
                                     for k, v in o.items()} for o in others]
-        bwd = bench_backward(T, W, args.steps, args.warmup)
+    if not args.quick:
+        bwd = _leg(result, "backward", lambda: bench_backward(T, W, args.steps, args.warmup))
+    if not args.quick and bwd is not None:
         for b in bwd:
             log(f"backward {b['workload']}: {b['avg_ms']*1e3:.1f} us, {b['tflops']:.1f} TFLOP/s "
                 f"(median {b['median_ms']*1e3:.1f} us)")
@@ -628,8 +648,8 @@ def main():
             f"host cores ({cb['sample']})")
         cb["value"] = round(cb["value"], 6)
         if not args.quick:
-            cb["other_workloads"] = cpu_oracle_samples()
-            for o in cb["other_workloads"]:
+            cb["other_workloads"] = _leg(cb, "other_workloads", cpu_oracle_samples) or cb.get("other_workloads", [])
+            for o in (cb["other_workloads"] if isinstance(cb["other_workloads"], list) else []):
                 log(f"cpu oracle {o['workload']}: {o['seconds']} s, {o['tflops']:.4f} TFLOP/s "
                     f"({o['sample']})")
         result["cpu_baseline"] = cb
