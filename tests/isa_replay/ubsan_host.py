@@ -20,7 +20,6 @@ from __future__ import annotations
 import ctypes
 import glob
 import json
-import math
 import os
 import random
 import subprocess
