@@ -283,6 +283,61 @@ def test_forward_replays_clean(case):
     assert_close(o.to(torch.float64).numpy(), lse.numpy(), ro, rl, name)
 
 
+
+def _wide_rows(g, B, H, N, D, n_stride):
+    """A [B, H, N, D] bf16 tensor whose rows lie n_stride elements apart (heads interleaved
+    inside a row): storage of about N * n_stride elements, of which only the logical ones
+    are ever written, so the untouched pages cost no memory."""
+    t = torch.empty_strided((B, H, N, D), (N * n_stride, D, n_stride, 1), dtype=torch.bfloat16)
+    t.copy_(W.randn_bf16(g, (B, H, N, D)))
+    return t
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+@pytest.mark.parametrize("D", [64, 128])
+def test_largest_row_stride_replays_clean(D):
+    """Row strides of 2^24 - 8 elements, the largest the boundary accepts for streamed
+    tiles: the copies of a 128-row tile then span almost 2^32 bytes, the limit of the
+    kernels' 32-bit tile offsets.  attn_fwd (fwd_kernel at D=64, the ping-pong kernel at
+    D=128) and attn_bwd (all three kernels; Q and dO with the same stride) replay without a
+    fault, race or lane-mask note, within the oracle bars."""
+    from isa_replay.host import Replay
+    from tiled_attention_attn_amd import _lib
+    B, H, N, ns = 1, 2, 200, 2**24 - 8
+    g = W.generator(D)
+    q, k, v, do = (_wide_rows(g, B, H, N, D, ns) for _ in range(4))
+    scale = 1.0 / math.sqrt(D)
+    desc = _lib.attn_mask_desc(flags=1, window_left=-1, window_right=-1)
+    mod = M.causal(N, N)
+    rp = Replay(("fwd", "fwd_pp", "bwd"))
+    o = torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16)
+    lse = torch.full((B, H, N), float("nan"))
+    rp.register(q=q, k=k, v=v, do=do, o=o, lse=lse)
+    assert rp.lib.attn_fwd(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                           o.data_ptr(), _strides(o), lse.data_ptr(), B, H, H, N, N, D, 0, scale,
+                           ctypes.byref(desc), None, None) == 0
+    rp.run()
+    assert not rp.notes, rp.notes
+    f64 = lambda x: x.to(torch.float64).numpy()  # noqa: E731
+    ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
+    assert_close(f64(o), lse.numpy(), ro, rl, f"row stride 2^24 - 8, D={D}")
+
+    dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16) for _ in range(3))
+    ws = torch.zeros(max(int(rp.lib.attn_bwd_workspace_bytes(B, H, N)) // 4, 1))
+    rp.register(dq=dq, dk=dk, dv=dv, ws=ws)
+    assert rp.lib.attn_bwd(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                           o.data_ptr(), _strides(o), do.data_ptr(), _strides(do), lse.data_ptr(),
+                           dq.data_ptr(), _strides(dq), dk.data_ptr(), _strides(dk), dv.data_ptr(), _strides(dv),
+                           B, H, H, N, N, D, 0, scale, ctypes.byref(desc), None, ws.data_ptr(), ws.numel() * 4,
+                           None) == 0
+    rp.run()
+    assert not rp.notes, rp.notes
+    rq, rk, rv, (mq, mk, mv) = OBW.attention_bwd(f64(q), f64(k), f64(v), f64(do), scale, mod, row_block=256,
+                                                 bound=True, o_used=f64(o))
+    _check_grad(dq, rq, mq, "dQ")
+    _check_grad(dk, rk, mk, "dK")
+    _check_grad(dv, rv, mv, "dV")
+
 # SQ counters per dispatch, read with rocprofv3 --pmc on an MI355X for the causal
 # 2x16x4096x64 prefill (fwd_kernel<64>) and the paged decode (decode_kernel<128>); both
 # dispatches ran 2048 waves.  Values as profiles/sq_counters_causal_b2h16n4096d64_and_decode.md
