@@ -338,6 +338,52 @@ def test_largest_row_stride_replays_clean(D):
     _check_grad(dk, rk, mk, "dK")
     _check_grad(dv, rv, mv, "dV")
 
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_paged_decode_pool_beyond_4gib_replays_clean():
+    """A page pool of 4.6 GB (140000 pages of [16, 8, 128] bf16) whose used pages all lie
+    past its first 4 GiB: the decode kernel's page addresses must be 64-bit.  Only the used
+    pages are ever written, so the rest of the pool costs no memory.  Split-KV + combine
+    replay without a fault, race or lane-mask note, and O / LSE match the oracle's paged
+    gather within the GPU tests' bars."""
+    from isa_replay.host import Replay
+    from oracle import paged as OP
+    B, Hq, Hkv, Lq, D, ps, S, P = 2, 16, 8, 4, 128, 16, 3, 140_000
+    sl = [300, 170]
+    g = W.generator(4)
+    per_seq = (max(sl) + ps - 1) // ps
+    first = P - 2000                                   # byte offset of page `first` > 2^32
+    assert first * ps * Hkv * D * 2 > 2**32
+    bt = (first + torch.randperm(2000, generator=g)[: B * per_seq]).reshape(B, per_seq).to(torch.int32)
+    q = W.randn_bf16(g, (B, Hq, Lq, D))
+    kp = torch.empty((P, ps, Hkv, D), dtype=torch.bfloat16)
+    vp = torch.empty((P, ps, Hkv, D), dtype=torch.bfloat16)
+    for pool in (kp, vp):
+        pool[bt.flatten().long()] = W.randn_bf16(g, (B * per_seq, ps, Hkv, D))
+    lens = torch.tensor(sl, dtype=torch.int32)
+    ws_o = torch.full((B, Hq, Lq, S, D), float("nan"))
+    ws_l = torch.full((B, Hq, Lq, S), float("nan"))
+    o = torch.full((B, Hq, Lq, D), float("nan"), dtype=torch.bfloat16)
+    lse = torch.full((B, Hq, Lq), float("nan"))
+    rp = Replay(("decode",))
+    rp.register(q=q, kp=kp, vp=vp, bt=bt, lens=lens, ws_o=ws_o, ws_l=ws_l, o=o, lse=lse)
+    scale = 1.0 / math.sqrt(D)
+    assert rp.lib.attn_decode_splitkv(q.data_ptr(), _strides(q), kp.data_ptr(), vp.data_ptr(), P, bt.data_ptr(),
+                                      bt.stride(0), lens.data_ptr(), per_seq, B, Hq, Hkv, Lq, D, 0, ps, S, scale,
+                                      None, None, ws_o.data_ptr(), ws_l.data_ptr(), None) == 0
+    assert rp.lib.attn_decode_combine(ws_o.data_ptr(), ws_l.data_ptr(), B, Hq, Lq, S, D, 0, o.data_ptr(),
+                                      _strides(o), lse.data_ptr(), None) == 0
+    rp.run()
+    assert not rp.notes, rp.notes
+    used_k = kp[first:].to(torch.float64).numpy()       # the oracle gathers from the used part
+    used_v = vp[first:].to(torch.float64).numpy()
+    bt_used = (bt - first).numpy()
+    for b in range(B):
+        kl = OP.gather(used_k, bt_used, b, sl[b])[None]
+        vl = OP.gather(used_v, bt_used, b, sl[b])[None]
+        ro, rl = oracle.attention(q[b:b + 1].to(torch.float64).numpy(), kl, vl, scale, M.causal(Lq, sl[b]))
+        assert_close(o[b:b + 1].to(torch.float64).numpy(), lse[b:b + 1].numpy(), ro, rl, f"sequence {b}")
+
 # SQ counters per dispatch, read with rocprofv3 --pmc on an MI355X for the causal
 # 2x16x4096x64 prefill (fwd_kernel<64>) and the paged decode (decode_kernel<128>); both
 # dispatches ran 2048 waves.  Values as profiles/sq_counters_causal_b2h16n4096d64_and_decode.md
