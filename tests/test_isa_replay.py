@@ -299,8 +299,8 @@ def test_largest_row_stride_replays_clean(D):
     """Row strides of 2^24 - 8 elements, the largest the boundary accepts for streamed
     tiles: the copies of a 128-row tile then span almost 2^32 bytes, the limit of the
     kernels' 32-bit tile offsets.  attn_fwd (fwd_kernel at D=64, the ping-pong kernel at
-    D=128) and attn_bwd (all three kernels; Q and dO with the same stride) replay without a
-    fault, race or lane-mask note, within the oracle bars."""
+    D=128), attn_fwd_blockmask and attn_bwd (all three kernels; Q and dO with the same
+    stride) replay without a fault, race or lane-mask note, within the oracle bars."""
     from isa_replay.host import Replay
     from tiled_attention_attn_amd import _lib
     B, H, N, ns = 1, 2, 200, 2**24 - 8
@@ -309,7 +309,7 @@ def test_largest_row_stride_replays_clean(D):
     scale = 1.0 / math.sqrt(D)
     desc = _lib.attn_mask_desc(flags=1, window_left=-1, window_right=-1)
     mod = M.causal(N, N)
-    rp = Replay(("fwd", "fwd_pp", "bwd"))
+    rp = Replay(("fwd", "fwd_pp", "bwd", "blockmask"))
     o = torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16)
     lse = torch.full((B, H, N), float("nan"))
     rp.register(q=q, k=k, v=v, do=do, o=o, lse=lse)
@@ -321,6 +321,25 @@ def test_largest_row_stride_replays_clean(D):
     f64 = lambda x: x.to(torch.float64).numpy()  # noqa: E731
     ro, rl = oracle.attention(f64(q), f64(k), f64(v), scale, mod)
     assert_close(f64(o), lse.numpy(), ro, rl, f"row stride 2^24 - 8, D={D}")
+
+    # the BlockMask kernel on the same tensors: every tile PARTIAL under the causal predicate
+    nt = (N + 127) // 128
+    tm = torch.ones(1, 1, nt, nt, dtype=torch.uint8)
+    lists = [torch.zeros(1, 1, nt, dtype=torch.int32), torch.zeros(1, 1, nt, nt, dtype=torch.int32),
+             torch.zeros(1, 1, nt, dtype=torch.int32), torch.zeros(1, 1, nt, nt, dtype=torch.int32)]
+    o_bm = torch.full_like(o, float("nan"))
+    lse_bm = torch.full_like(lse, float("nan"))
+    rp.register(tm=tm, o_bm=o_bm, lse_bm=lse_bm, **{f"lists{i}": t for i, t in enumerate(lists)})
+    bm = _lib.attn_blockmask(Bm=1, Hm=1, nQt=nt, nKt=nt, part_num=lists[0].data_ptr(),
+                             part_idx=lists[1].data_ptr(), full_num=lists[2].data_ptr(),
+                             full_idx=lists[3].data_ptr())
+    assert rp.lib.attn_build_blockmask(None, tm.data_ptr(), B, N, N, ctypes.byref(bm), None) == 0
+    assert rp.lib.attn_fwd_blockmask(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
+                                     _strides(v), o_bm.data_ptr(), _strides(o_bm), lse_bm.data_ptr(), B, H, H, N, N,
+                                     D, 0, scale, ctypes.byref(desc), None, ctypes.byref(bm), None) == 0
+    rp.run()
+    assert not rp.notes, rp.notes
+    assert_close(f64(o_bm), lse_bm.numpy(), ro, rl, f"BlockMask, row stride 2^24 - 8, D={D}")
 
     dq, dk, dv = (torch.full((B, H, N, D), float("nan"), dtype=torch.bfloat16) for _ in range(3))
     ws = torch.zeros(max(int(rp.lib.attn_bwd_workspace_bytes(B, H, N)) // 4, 1))
