@@ -489,6 +489,42 @@ def test_no_kernel_branches_on_a_lane_mask_from_a_lane_by_lane_loop():
     assert not any(found.values()), {n: s for n, s in found.items() if s}
 
 
+
+# Scratch bytes a lane may spill, per kernel family with a score change (SM): the only
+# variants whose registers overflow at their two-waves-per-SIMD budget.  Every other kernel
+# must not spill.
+_SPILL_LIMITS = {
+    ("fwd_kernel<64,", True): 140,
+    ("bwd_kv_kernel<64,", True): 224,
+    ("bwd_q_kernel<128,", True): 24,
+}
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_every_kernel_keeps_the_lds_rule_and_the_recorded_spills():
+    """From the compiled kernel descriptors of every kernel: no work group uses more than
+    72 KB of LDS (two groups per CU, and the footprint rule of every kernel's LDS
+    declaration), and only the score-change variants listed above spill, by at most the
+    listed bytes.  A kernel change that starts a new spill, or grows one, fails here."""
+    import glob
+    from isa_replay.host import Kernels, build
+    from isa_replay.mix import demangle
+    from tiled_attention_attn_amd import build as B
+    names = tuple(os.path.basename(p)[:-4] for p in sorted(glob.glob(os.path.join(B.CSRC, "*.hip")))
+                  if not p.endswith("attn_api.hip"))
+    _, asm = build(names)
+    kernels = Kernels(list(asm.values()))
+    assert len(kernels.desc) > 60
+    for name, d in kernels.desc.items():
+        k = demangle(name)
+        assert d["group_segment_fixed_size"] <= 72 * 1024, (k, d["group_segment_fixed_size"])
+        # the SM template argument is the third of fwd_kernel / bwd_*_kernel and the last of decode
+        args = [a.strip() for a in k[k.find("<") + 1:k.rfind(">")].split(",")] if "<" in k else []
+        sm = len(args) >= 3 and args[2] == "true" if k.startswith(("bwd_kv", "bwd_q")) else (
+            len(args) >= 4 and args[3] == "true" if k.startswith("fwd_kernel") else False)
+        limit = next((v for (pre, s_), v in _SPILL_LIMITS.items() if k.startswith(pre) and s_ == sm), 0)
+        assert d["private_segment_fixed_size"] <= limit, (k, d["private_segment_fixed_size"], limit)
+
 _LOOP_ASM = """\
 probe:
 \ts_mov_b64 s[8:9], 0
