@@ -202,7 +202,8 @@ typedef struct attn_blockmask {
 } attn_blockmask;
 
 /* Bytes of device memory the four arrays of one attn_blockmask need in total
- * (the caller allocates them; 0 on invalid sizes). */
+ * (the caller allocates them; 0 on invalid sizes, and when the count would not
+ * fit a size_t). */
 size_t attn_blockmask_bytes(int Bm, int Hm, int nQt, int nKt);
 
 /* attn_build_blockmask: fills `out` (whose pointers and Bm, Hm, nQt, nKt the
@@ -273,7 +274,8 @@ int attn_decode_splitkv(const void* q, const int64_t q_stride[3],
 /* attn_decode_combine: O = sum_s exp(LSE_s - LSE) O_s with
  * LSE = log sum_s exp(LSE_s) (max-shifted); splits with LSE_s = -inf weigh 0.
  *   o   [B, Hq, Lq, D] of `dtype` (strides (b, h, n)); lse float [B, Hq, Lq] or NULL.
- * o and ws_o must be 16-byte aligned (ATTN_ERR_ALIGN otherwise).
+ * o and ws_o must be 16-byte aligned (ATTN_ERR_ALIGN otherwise).  B * Hq * Lq
+ * rows must stay below 2^31 - 3 (ATTN_ERR_SHAPE otherwise).
  */
 int attn_decode_combine(const float* ws_o, const float* ws_lse,
                         int B, int Hq, int Lq, int S, int D, int dtype,
@@ -304,7 +306,9 @@ int attn_decode_noalloc(const void* q, const int64_t q_stride[3],
                         float* lse, hipStream_t stream);
 size_t attn_decode_noalloc_max_bytes(void);
 
-/* Workspace sizes of attn_decode_splitkv in bytes (0 on invalid sizes). */
+/* Workspace sizes of attn_decode_splitkv in bytes (0 on invalid sizes, and when
+ * the count would not fit a size_t; attn_decode_splitkv refuses such shapes with
+ * ATTN_ERR_SHAPE). */
 size_t attn_decode_ws_o_bytes(int B, int Hq, int Lq, int D, int num_splits);
 size_t attn_decode_ws_lse_bytes(int B, int Hq, int Lq, int num_splits);
 
@@ -320,7 +324,8 @@ int attn_decode_num_splits(int B, int Hkv, int max_pages, int num_cus);
  * attn_fwd, on contiguous (non-paged) K/V.
  *
  * The split-KV path is taken when all G * Nq query rows of a KV head fit one
- * 64-row group (G = Hq / Hkv, so G * Nq <= 64) and Nk >= 512.  It runs the
+ * 64-row group (G = Hq / Hkv, so G * Nq <= 64), Nk >= 512 and the combine's
+ * B * Hq * Nq rows stay below 2^31 - 3.  It runs the
  * split-KV kernel over K/V in place and
  * then the combine: K/V are read once per KV head rather than once per query
  * head, and the key splits fill the GPU.  Every other shape runs attn_fwd.
@@ -435,7 +440,8 @@ int attn_bwd_blockmask(const void* q, const int64_t q_stride[3],
  * (qt, kt) is PARTIAL / FULL in `bm`.  out->Bm / Hm must equal bm's, out->nQt
  * = bm->nKt and out->nKt = bm->nQt; its arrays are caller-allocated
  * (attn_blockmask_bytes(Bm, Hm, bm->nKt, bm->nQt)).  map_tmp is device memory
- * of at least Bm * Hm * nQt * nKt bytes, overwritten (a class map).
+ * of at least Bm * Hm * nQt * nKt bytes, overwritten (a class map); a count
+ * that would not fit a size_t gives ATTN_ERR_BLOCKMASK.
  */
 int attn_blockmask_transpose(const attn_blockmask* bm, attn_blockmask* out, uint8_t* map_tmp,
                              size_t map_tmp_bytes, hipStream_t stream);

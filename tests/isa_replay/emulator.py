@@ -11,7 +11,8 @@ Memory results are held back until an s_waitcnt retires them (vector memory and 
 scalar memory each complete in issue order), so the replay sees what the hardware
 guarantees and nothing more.  It raises
 
-  * ``Fault`` for a global, scratch or LDS access outside its allocation;
+  * ``Fault`` for a global, scratch or LDS access outside its allocation, and for an
+    LDS-DMA copy at or above ``LDS_COPY_LIMIT``;
   * ``Hazard`` for a read or overwrite of a register whose load is still in flight, an
     LDS access to bytes an unfinished copy of the same wave is writing, and two waves
     touching the same LDS byte (at least one writing) between two barriers, where a
@@ -33,6 +34,10 @@ M32 = 0xFFFFFFFF
 M64 = 0xFFFFFFFFFFFFFFFF
 LANES = 64
 U32, U64, I32 = np.uint32, np.uint64, np.int32
+# Asynchronous LDS copies of the library target only the first 64 KB of a work group's LDS
+# (the rule that followed a GPU fault of a build copying into 64-128 KB); a replayed copy
+# above it is reported as a fault.
+LDS_COPY_LIMIT = 64 * 1024
 
 
 class Fault(Exception):
@@ -1241,6 +1246,8 @@ class Semantics:
             raw = self.m.mem.read(int(addr[l]), 16).copy()
             la = base + 16 * int(l)
             self.m.lds_check(w, la, 16)
+            if la + 16 > LDS_COPY_LIMIT:
+                raise Fault(f"LDS copy to {la:#x}: the library keeps its copies below {LDS_COPY_LIMIT:#x}")
             copies.append((la, raw))
             span.append((la, 16, True))
         op = {"smem": False, "writes": [], "lds_copy": copies, "lds_span": span}

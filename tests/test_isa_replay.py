@@ -607,3 +607,41 @@ def test_replay_flags_out_of_bounds_and_unwaited_loads():
         _probe("s_waitcnt vmcnt(0)", 63)          # lane 63 reads one word past the buffer
     with pytest.raises(E.Hazard, match="outstanding"):
         _probe("v_mov_b32_e32 v5, v4", 64)        # uses the load's register before its wait
+
+
+
+_DMA_ASM = """\
+probe:
+\ts_load_dwordx2 s[4:5], s[0:1], 0x0
+\tv_lshlrev_b32_e32 v1, 4, v0
+\ts_mov_b32 m0, {m0}
+\ts_waitcnt lgkmcnt(0)
+\ts_nop 0
+\tglobal_load_lds_dwordx4 v1, s[4:5]
+\ts_waitcnt vmcnt(0)
+\ts_endpgm
+.Lfunc_end0:
+"""
+
+
+def test_replay_flags_lds_copies_above_64_kib():
+    """The replay enforces the LDS copy rule: one wave's 1 KB LDS-DMA copy ending at the
+    64 KB mark runs, the same copy starting there is a fault (in a 128 KB allocation, so
+    only the rule, not the bounds check, can object)."""
+    from isa_replay import emulator as E
+
+    def run(m0):
+        mem = E.Memory()
+        buf = mem.alloc(np.arange(256, dtype=np.uint32).tobytes(), "buffer")
+        ka = mem.alloc(np.array([buf], dtype=np.uint64).tobytes(), "kernarg")
+        with tempfile.NamedTemporaryFile("w", suffix=".s", delete=False) as fh:
+            fh.write(_DMA_ASM.format(m0=hex(m0)))
+        try:
+            m = E.Machine(fh.name, "probe", mem, ka, 128 * 1024, 64)
+            m.run_group((0, 0, 0), [0])
+        finally:
+            os.unlink(fh.name)
+
+    run(0x10000 - 1024)
+    with pytest.raises(E.Fault, match="copies below"):
+        run(0x10000)
