@@ -12,12 +12,15 @@ def pytest_configure(config):
 
 def _gpu_order(item):
     """GPU tests of the forward, BlockMask-builder and decode kernels run first, then the
-    dense backward, the backward with score changes, the BlockMask backward, and the
-    allocation-free decode test last.  A GPU fault ends the whole test process, so kernels
+    dense backward, the backward with score changes, the BlockMask backward, the address-
+    limit cases (multi-GB strided tensors and page pools), and the allocation-free decode
+    test last.  A GPU fault ends the whole test process, so kernels
     with a longer GPU record are checked before newer ones."""
     base = os.path.basename(str(item.fspath))
     if base.startswith("test_zz_"):
         return 4
+    if base == "test_gpu_large_addresses.py":
+        return 3.5
     name = base + "::" + item.name
     if "backward_blockmask" in name:
         return 3

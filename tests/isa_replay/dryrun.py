@@ -1,0 +1,104 @@
+"""Dry run of GPU test functions on the CPU, through the compiled kernels.
+
+``python -m isa_replay.dryrun <test module> <function>[[k]] ...`` (from ``tests/``; every
+parametrization of the function, or only its k-th) imports a GPU test module with the package's Python binding intact, but:
+
+  * the binding's library is the host-only copy whose kernel launches are recorded
+    (``host.Replay``), and every tensor whose pointer the binding passes is registered
+    with the emulator as device memory;
+  * tensors live on the CPU (the module's ``DEV`` becomes "cpu", BlockMask buffers too);
+  * ``torch.cuda.synchronize()`` runs the launches recorded so far on the emulator, work
+    group by work group, with its bounds, race and lane-mask checks.
+
+So a GPU test's own code -- shapes, binding calls, oracle comparisons -- runs end to end
+against the kernels' gfx950 assembly, and must pass as it would on the GPU.  Meant for
+small GPU test cases: the emulator runs about a million wave instructions a minute.
+This process patches torch.cuda, so run it in a process of its own.
+"""
+from __future__ import annotations
+
+import importlib
+import sys
+
+
+def main(argv):
+    import torch
+    torch.cuda.is_available = lambda: True  # the test module imports the binding
+    from .host import Replay
+    from tiled_attention_attn_amd import _lib as L
+
+    rp = Replay(("fwd", "fwd_pp", "bwd", "blockmask", "decode", "decode_noalloc"))
+    seen = set()
+
+    def reg(t):
+        if t is not None and t.untyped_storage().data_ptr() not in seen:
+            seen.add(t.untyped_storage().data_ptr())
+            rp.register(**{f"tensor{len(seen)}": t})
+
+    ptr, struct, init = L._ptr, L.BlockMask.struct, L.BlockMask.__init__
+
+    def ptr_reg(t):
+        reg(t)
+        return ptr(t)
+
+    def struct_reg(self):
+        for t in (self.part_num, self.part_idx, self.full_num, self.full_idx):
+            reg(t)
+        return struct(self)
+
+    def init_cpu(self, Bm, Hm, Nq, Nk, device="cuda"):
+        init(self, Bm, Hm, Nq, Nk, device="cpu")
+
+    def synchronize(*_):
+        rp.run()
+        if rp.notes:
+            raise AssertionError(f"replay notes: {rp.notes}")
+
+    L._ptr, L.BlockMask.struct, L.BlockMask.__init__ = ptr_reg, struct_reg, init_cpu
+    L._on_device = lambda *a: None
+    L._stream = lambda s: None
+    L._lib = rp.lib
+    torch.cuda.synchronize = synchronize
+    torch.cuda.empty_cache = lambda: None
+
+    import pytest
+    mod = importlib.import_module(argv[0])
+    mod.DEV = "cpu"
+    for spec in argv[1:]:
+        name, _, sel = spec.partition("[")
+        fn = getattr(mod, name)
+        calls = _parameter_sets(fn)
+        if sel:
+            calls = [calls[int(sel.rstrip("]"))]]
+        for label, kwargs in calls:
+            try:
+                fn(**kwargs)
+                synchronize()
+                print(f"dry run passed: {argv[0]}::{name}{label}", flush=True)
+            except pytest.skip.Exception as e:
+                print(f"dry run skipped: {argv[0]}::{name}{label} ({e})", flush=True)
+
+
+def _parameter_sets(fn):
+    """(label, keyword arguments) of every parametrization of a test function, in the
+    order pytest would make them (the last decorator's argument varies fastest)."""
+    import itertools
+    marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+    axes = []
+    for m in reversed(marks):  # decorators apply bottom-up
+        names = [n.strip() for n in m.args[0].split(",")] if isinstance(m.args[0], str) else list(m.args[0])
+        ids = m.kwargs.get("ids")
+        vals = list(m.args[1])
+        axes.append([(ids[i] if ids else str(i), dict(zip(names, v if len(names) > 1 else (v,))))
+                     for i, v in enumerate(vals)])
+    out = []
+    for combo in itertools.product(*axes):
+        kw = {}
+        for _, d in combo:
+            kw.update(d)
+        out.append(("[" + "-".join(lbl for lbl, _ in combo) + "]" if combo else "", kw))
+    return out or [("", {})]
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

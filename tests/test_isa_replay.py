@@ -645,3 +645,22 @@ def test_replay_flags_lds_copies_above_64_kib():
     run(0x10000 - 1024)
     with pytest.raises(E.Fault, match="copies below"):
         run(0x10000)
+
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_gpu_address_limit_tests_dry_run_on_the_cpu():
+    """tests/test_gpu_large_addresses.py, the GPU tests themselves, run on the CPU through
+    isa_replay.dryrun: the binding's calls reach the compiled kernels' replay, and every
+    comparison of the test file passes (row stride 2^24 - 8 forward, BlockMask and
+    backward at D=64 and 128; paged decode over a 4.6 GB pool)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, PYTHONPATH=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-m", "isa_replay.dryrun", "test_gpu_large_addresses",
+                        "test_largest_row_stride_forward", "test_largest_row_stride_backward",
+                        "test_paged_decode_pool_beyond_4gib"],
+                       cwd=os.path.dirname(os.path.abspath(__file__)), env=env, capture_output=True, text=True,
+                       timeout=1200)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert r.stdout.count("dry run passed") == 5, r.stdout
