@@ -38,6 +38,9 @@ U32, U64, I32 = np.uint32, np.uint64, np.int32
 # (the rule that followed a GPU fault of a build copying into 64-128 KB); a replayed copy
 # above it is reported as a fault.
 LDS_COPY_LIMIT = 64 * 1024
+# Initial byte of every lane's private (scratch) memory.  A read of scratch bytes never
+# written is noted; replaying with another fill shows whether such a read can matter.
+PRIV_FILL = 0
 
 
 class Fault(Exception):
@@ -270,7 +273,7 @@ class Wave:
         self.pend = {}      # (kind, reg) -> youngest outstanding op writing it
         self.maskdef = {}   # SGPR pair / 'vcc' -> (EXEC, line) of the compare that made it
         n = max(priv_bytes, 4)
-        self.priv = np.zeros((LANES, n), dtype=np.uint8)
+        self.priv = np.full((LANES, n), PRIV_FILL, dtype=np.uint8)
         self.priv_written = np.zeros((LANES, n), dtype=bool)
 
     # ---- hazards of outstanding loads
