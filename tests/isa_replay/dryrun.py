@@ -84,6 +84,17 @@ def main(argv):
     L._lib = rp.lib
     torch.cuda.synchronize = synchronize
     torch.cuda.empty_cache = lambda: None
+    # tests that call the C ABI directly pass the current stream's handle: the null stream
+    torch.cuda.current_stream = lambda *a: type("Stream", (), {"cuda_stream": 0})()
+    # and their tensors: any tensor whose address is taken counts as device memory
+    data_ptr = torch.Tensor.data_ptr
+
+    def data_ptr_reg(t):
+        if t.numel():
+            reg(t)
+        return data_ptr(t)
+
+    torch.Tensor.data_ptr = data_ptr_reg
 
     import pytest
     mod = importlib.import_module(argv[0])
