@@ -664,3 +664,21 @@ def test_gpu_address_limit_tests_dry_run_on_the_cpu():
                        timeout=1200)
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
     assert r.stdout.count("dry run passed") == 5, r.stdout
+
+
+
+@pytest.mark.skipif(not HAVE_HIPCC, reason="needs hipcc to compile the kernels' assembly")
+def test_score_change_backward_that_faulted_dry_runs_on_the_cpu():
+    """test_gpu_score_mod.py::test_backward_score_mod[alibi_sym_window_d64], the GPU case
+    that faulted before the dK/dV row-search fix, run as written on the CPU through
+    isa_replay.dryrun: attn_fwd then attn_bwd with symmetric ALiBi and a bias table at
+    D=64, every gradient within the test's bar (scratch filled with 0x7F)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, PYTHONPATH=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    r = subprocess.run([sys.executable, "-m", "isa_replay.dryrun", "test_gpu_score_mod",
+                        "test_backward_score_mod[2]"],
+                       cwd=os.path.dirname(os.path.abspath(__file__)), env=env, capture_output=True, text=True,
+                       timeout=1200)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert "dry run passed: test_gpu_score_mod::test_backward_score_mod[alibi_sym_window_d64]" in r.stdout, r.stdout
